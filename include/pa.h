@@ -1,0 +1,237 @@
+/*
+ * pa.h -- C ABI of the paged KV cache library for MI355X (gfx950).
+ *
+ * A KV cache stored in fixed-size physical blocks that need not be contiguous,
+ * reached through a per-sequence block table, with blocks handed out on demand
+ * and shared between sequences with copy-on-write.  Pages this follows:
+ *
+ *   [studynote 223] "KV Cache PagedAttention" (agnusdei1207 brainscience study note 223)
+ *   [studynote 528] "vLLM PagedAttention KV cache optimization" (agnusdei1207 study note 528)
+ *   [ch.09]         "09. PagedAttention" (119-ai-studio LLM inference guide, chapter 9)
+ *   [velog]         "Paged Attention" (velog.io/@junegood)
+ *
+ * Conventions for every call:
+ *   - Return value: PA_OK (0) or a negative pa_status.  Nothing is printed and no
+ *     C++ exception crosses this boundary.
+ *   - Host-side calls (allocator, sizes, layout) touch no GPU and may run on a
+ *     machine without one.
+ *   - Device calls take DEVICE pointers the caller owns (allocated by the caller,
+ *     e.g. through torch); the library never allocates or frees device memory.
+ *     They are asynchronous on `stream` (a hipStream_t; NULL = the null stream),
+ *     never synchronize, and return PA_ERR_HIP if a launch fails.  Arguments that
+ *     live on the host are validated before anything is launched; values that
+ *     live on the device (block tables, lengths, slots) are bounds-checked by the
+ *     kernels, which never read or write outside the buffers described here.
+ *   - The calling thread's current HIP device is the one used.
+ *
+ * Cache layout (both pools are flat arrays of the cache dtype; H = kv heads,
+ * bs = block_size, D = head_dim; slot s is token offset s % bs of block s / bs):
+ *   K pool element (block b, head g, offset o, channel d) at ((b*H + g)*bs + o)*D + d
+ *   V pool element (block b, head g, offset o, channel d) at ((b*H + g)*D + d)*bs + o
+ * so one (block, head) tile is contiguous in each pool: K as bs token rows of
+ * D channels, V as D channel rows of bs tokens.  pa_kv_offset() evaluates this.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+    PA_OK = 0,
+    PA_ERR_INVALID_ARG = -1,   /* a pointer, size or shape is invalid */
+    PA_ERR_OUT_OF_BLOCKS = -2, /* the pool has too few free blocks; nothing changed */
+    PA_ERR_BAD_BLOCK = -3,     /* block id out of range or not allocated */
+    PA_ERR_BAD_SEQ = -4,       /* unknown sequence id */
+    PA_ERR_HIP = -5,           /* a HIP runtime call or kernel launch failed */
+    PA_ERR_UNSUPPORTED = -6,   /* valid, but a shape this build has no kernel for */
+    PA_ERR_NO_MEMORY = -7      /* host allocation failed */
+} pa_status;
+
+typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* Shape of one paged cache (one layer): num_blocks physical blocks of
+ * block_size token slots, num_kv_heads heads of head_dim channels, stored as
+ * kv_dtype (a pa_dtype). */
+typedef struct pa_cache_desc {
+    int32_t num_blocks;
+    int32_t block_size;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t kv_dtype;
+} pa_cache_desc;
+
+/* ---- library ---------------------------------------------------------------- */
+
+/* Human-readable name of a pa_status value (static storage). */
+const char* pa_status_string(int status);
+
+/* ABI version of this header: (major << 16) | minor. */
+int32_t pa_version(void);
+
+/* ---- layout (host) ----------------------------------------------------------- */
+
+/* Bytes of ONE pool (K or V) for this shape; 0 if desc is invalid. */
+size_t pa_cache_pool_bytes(const pa_cache_desc* desc);
+
+/* Element offset of (slot, head, dim) in the K pool (which = 0) or the V pool
+ * (which = 1), per the layout above.  -1 for an invalid argument.  The physical
+ * block of a slot is a design freedom the pages leave open ([ch.09] "해법":
+ * any free physical block may hold a logical block); the arrangement inside a
+ * block is this library's. */
+int64_t pa_kv_offset(const pa_cache_desc* desc, int32_t which, int64_t slot, int32_t head,
+                     int32_t dim);
+
+/* ---- block allocator (host) ----------------------------------------------------
+ * [velog] "구현 세부사항 / 메모리 할당자": allocate_block() returns a free physical
+ * block id and free_block(id) returns a block for reuse.  [studynote 223]
+ * section II figure and [velog] "작동 예시": a sequence takes a new block only when
+ * its last block is full (tokens 1, 17, 33, ... at 16 tokens per block).
+ * [studynote 223] section II copy-on-write paragraph and [velog] "메모리 공유
+ * (Copy-on-Write)": sequences with a common prefix share its blocks; a writer
+ * into a shared block first gets a private copy.
+ *
+ * Rules of this implementation: the free list is FIFO, seeded with
+ * initial_free_order (NULL = 0..N-1); a block whose reference count drops to
+ * zero goes to its tail.  Every call is all-or-nothing.  Sequence ids are
+ * 0, 1, 2, ... in creation order and never reused.  An allocator is not
+ * thread-safe; distinct allocators are independent.  All outputs go to
+ * caller-owned host memory. */
+typedef struct pa_allocator pa_allocator;
+
+/* Create an allocator over num_blocks blocks of block_size tokens.
+ * initial_free_order: NULL or a permutation of 0..num_blocks-1 (copied).
+ * *out receives the handle (library-owned; release with pa_allocator_destroy). */
+int pa_allocator_create(int32_t num_blocks, int32_t block_size,
+                        const int32_t* initial_free_order, pa_allocator** out);
+void pa_allocator_destroy(pa_allocator* a);
+
+/* The pages' allocate_block(): pop the head of the free list, count = 1. */
+int pa_allocate_block(pa_allocator* a, int32_t* block_out);
+/* The pages' free_block(): drop one reference; at zero the block is free again.
+ * PA_ERR_BAD_BLOCK if the block is out of range or not allocated. */
+int pa_free_block(pa_allocator* a, int32_t block);
+/* Number of free blocks (>= 0), or a negative status. */
+int32_t pa_num_free(const pa_allocator* a);
+/* Reference count of a block (>= 0), or a negative status. */
+int32_t pa_refcount(const pa_allocator* a, int32_t block);
+
+/* New empty sequence. */
+int pa_seq_create(pa_allocator* a, int32_t* seq_out);
+/* New sequence sharing every block of `parent` (each block's count + 1). */
+int pa_seq_fork(pa_allocator* a, int32_t parent, int32_t* child_out);
+/* Grow `seq` by n_tokens (>= 0).  slot_mapping_out[i] (n_tokens entries, may be
+ * NULL when n_tokens == 0) receives the slot of position length+i, where
+ * slot = physical_block * block_size + position % block_size.  If the last
+ * block is partially filled and shared, it is first replaced by a fresh block
+ * and the pair (src, dst) is written to cow_pair_out[0..1]; *n_cow_out is 1 then,
+ * else 0.  The caller must copy src to dst (pa_copy_blocks) before writing the
+ * new tokens.  PA_ERR_OUT_OF_BLOCKS leaves everything unchanged. */
+int pa_seq_append_slots(pa_allocator* a, int32_t seq, int32_t n_tokens,
+                        int64_t* slot_mapping_out, int64_t* cow_pair_out, int32_t* n_cow_out);
+/* Make logical block `logical_index` of `seq` private: if it is shared, a
+ * fresh block replaces it and (src, dst) is written to cow_pair_out with
+ * *n_cow_out = 1; otherwise nothing changes and *n_cow_out = 0. */
+int pa_seq_cow_block(pa_allocator* a, int32_t seq, int32_t logical_index,
+                     int64_t* cow_pair_out, int32_t* n_cow_out);
+/* Release every block of `seq` (logical order) and forget the sequence. */
+int pa_seq_free(pa_allocator* a, int32_t seq);
+/* Tokens held by `seq` (>= 0), or a negative status. */
+int32_t pa_seq_length(const pa_allocator* a, int32_t seq);
+/* Copy the block table of `seq` into table_out (capacity `cap` entries);
+ * *n_out receives its length.  PA_ERR_INVALID_ARG if cap is too small. */
+int pa_seq_block_table(const pa_allocator* a, int32_t seq, int32_t* table_out, int32_t cap,
+                       int32_t* n_out);
+/* Block tables of n sequences as an int32 [n][max_blocks] row-major array padded
+ * with -1, plus their lengths in context_lens_out[n].  PA_ERR_INVALID_ARG if a
+ * sequence holds more than max_blocks blocks. */
+int pa_build_block_tables(const pa_allocator* a, const int32_t* seqs, int32_t n,
+                          int32_t max_blocks, int32_t* tables_out, int32_t* context_lens_out);
+
+/* ---- device operations ------------------------------------------------------------ */
+
+/* Scatter new tokens into their cache slots ([studynote 223] section II figure:
+ * a growing request's new KV goes into the block the table links in;
+ * [velog] "작동 예시").
+ *   k_cache, v_cache: device pools (layout above), written.
+ *   k_new, v_new:     device [num_tokens][num_kv_heads][head_dim], cache dtype.
+ *   slot_mapping:     device int64 [num_tokens]; a negative slot is padding and
+ *                     writes nothing; a slot >= num_blocks*block_size is ignored.
+ * Bit-exact copy: no arithmetic is applied to the values. */
+int pa_cache_write(void* k_cache, void* v_cache, const pa_cache_desc* desc, const void* k_new,
+                   const void* v_new, const int64_t* slot_mapping, int32_t num_tokens,
+                   void* stream);
+
+/* Copy-on-write block copy ([studynote 223] section II copy-on-write paragraph;
+ * [velog] "메모리 공유 (Copy-on-Write)"): for each pair, every head and slot of
+ * block src is copied to block dst, in both pools.
+ *   pairs_host: HOST int64 [n_pairs][2] = (src, dst), as the allocator emits them.
+ * PA_ERR_INVALID_ARG (nothing launched) if an id is out of range, a dst repeats,
+ * or a dst is also a src.  The ids travel in kernel arguments, so the call makes
+ * no host-to-device copy and needs no workspace. */
+int pa_copy_blocks(void* k_cache, void* v_cache, const pa_cache_desc* desc,
+                   const int64_t* pairs_host, int32_t n_pairs, void* stream);
+
+/* Workspace bytes pa_decode needs: room for the per-partition running max, sum
+ * and unnormalised output of every (sequence, query head, partition) when a
+ * sequence spans more than one partition; 0 when max_context_len fits in one.
+ * partition_size 0 means 512. */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t partition_size);
+
+/* Paged decode attention: one query token per sequence against its context,
+ * read block by block through its block table ([studynote 223] three-line summary
+ * item 3 and section II: attention over scattered blocks bound by the table;
+ * [ch.09] "해법": logical blocks look contiguous, physical ones are scattered).
+ * For query head h the result is softmax(scale * K q_h) V over positions
+ * 0..context_lens[s]-1 of kv head h / (num_q_heads / num_kv_heads).
+ *   out:          device [num_seqs][num_q_heads][head_dim] of out_dtype (PA_F32 or PA_BF16).
+ *   q:            device [num_seqs][num_q_heads][head_dim] in the cache dtype.
+ *   block_tables: device int32 [num_seqs][max_blocks_per_seq]; only the first
+ *                 ceil(L/block_size) entries of a row are read.
+ *   context_lens: device int32 [num_seqs]; L counts the newest token.
+ *   max_context_len: an upper bound of every L, used to size the grid.
+ *   partition_size: tokens per split-K partition (0 = 512); a multiple of 128
+ *                 and of block_size, at most 512.
+ *   workspace:    device scratch of >= pa_decode_workspace_bytes(...) bytes, or
+ *                 NULL when that is 0.
+ * Device-side checks: a row whose L is < 1 or > max_context_len, whose needed
+ * table entries leave [0, num_blocks), or whose L exceeds
+ * max_blocks_per_seq*block_size, produces NaN outputs instead of reading out of
+ * bounds.  Supported: head_dim 64 or 128, num_q_heads/num_kv_heads in 1..16,
+ * block_size 8..256 a power of two (fp32 caches: 4..256), cache PA_F32 or PA_BF16.
+ * Runs pa_decode_partitions then pa_decode_reduce. */
+int pa_decode(void* out, int32_t out_dtype, const void* q, const void* k_cache,
+              const void* v_cache, const pa_cache_desc* desc, const int32_t* block_tables,
+              int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+              int32_t num_q_heads, int32_t max_context_len, float scale, int32_t partition_size,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/* First half of pa_decode: one workgroup per (sequence, kv head, partition).
+ * Sequences with one partition get their final output written here; the
+ * others leave per-partition partials in the workspace for pa_decode_reduce.
+ * Same arguments and checks as pa_decode. */
+int pa_decode_partitions(void* out, int32_t out_dtype, const void* q, const void* k_cache,
+                         const void* v_cache, const pa_cache_desc* desc,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                         int32_t max_context_len, float scale, int32_t partition_size,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Second half of pa_decode: merge the partitions of every sequence that has
+ * more than one, rescaling each partition's sum by exp(its max - overall max).
+ * Arguments as in pa_decode (the same values must be passed to both halves). */
+int pa_decode_reduce(void* out, int32_t out_dtype, const int32_t* context_lens, int32_t num_seqs,
+                     int32_t num_q_heads, int32_t head_dim, int32_t max_context_len,
+                     int32_t partition_size, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

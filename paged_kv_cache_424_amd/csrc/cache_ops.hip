@@ -1,0 +1,145 @@
+// Cache write (scatter new tokens into their slots) and copy-on-write block copy.
+//
+// [studynote 223] "KV Cache PagedAttention", section II figure: a growing request's
+//   new KV is stored in whichever physical block its table links in next.
+// [velog] "Paged Attention", section 작동 예시: tokens fill block after block.
+// [studynote 223] section II copy-on-write paragraph; [velog] 메모리 공유
+//   (Copy-on-Write): a shared block is duplicated before one sharer diverges.
+//
+// Both kernels move raw bits (16/32-bit integers), so every value -- NaN
+// payloads included -- arrives unchanged.  Both are HBM-latency bound at the
+// sizes a decode step writes; they exist to be correct and cheap to launch.
+
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+// One thread per 4-byte word of a token's K row (2 bf16 or 1 fp32 element).
+// K rows are contiguous in the pool, so a wave stores 256 contiguous bytes;
+// V is channel-major inside a block, so each element is its own 2/4-byte store.
+template <typename W>   // W = uint16_t (bf16) or uint32_t (fp32): the element's bits
+__global__ __launch_bounds__(256) void cache_write_kernel(
+    W* __restrict__ kc, W* __restrict__ vc, const W* __restrict__ kn, const W* __restrict__ vn,
+    const int64_t* __restrict__ slots, int32_t num_tokens, int32_t H, int32_t D, int32_t bs,
+    int64_t num_slots) {
+    constexpr int E = 4 / sizeof(W);            // elements per 4-byte word
+    const int words = D / E;
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t total = static_cast<int64_t>(num_tokens) * H * words;
+    if (idx >= total) return;
+    const int wd = static_cast<int>(idx % words);
+    const int64_t th = idx / words;
+    const int g = static_cast<int>(th % H);
+    const int64_t t = th / H;
+    const int64_t slot = slots[t];
+    if (slot < 0 || slot >= num_slots) return;
+    const int64_t blk = slot / bs, off = slot % bs;
+    const int64_t src = (t * H + g) * D + static_cast<int64_t>(wd) * E;
+    const uint32_t word = *reinterpret_cast<const uint32_t*>(kn + src);
+    *reinterpret_cast<uint32_t*>(kc + ((blk * H + g) * bs + off) * D + static_cast<int64_t>(wd) * E) =
+        word;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int64_t d = static_cast<int64_t>(wd) * E + e;
+        vc[((blk * H + g) * D + d) * bs + off] = vn[src + e];
+    }
+}
+
+constexpr int kPairsPerLaunch = 128;
+
+struct CopyBatch {
+    int32_t src[kPairsPerLaunch];
+    int32_t dst[kPairsPerLaunch];
+};
+
+// grid = (pairs in batch, 2 pools, splits of the block tile).  A (block, all
+// heads) tile is contiguous in both pools; each workgroup copies 16-byte words
+// [split * per_split, ...) of it.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ kc,
+                                                          uint4* __restrict__ vc, CopyBatch b,
+                                                          int64_t tile_words, int64_t per_split) {
+    uint4* pool = blockIdx.y == 0 ? kc : vc;
+    const int64_t src = static_cast<int64_t>(b.src[blockIdx.x]) * tile_words;
+    const int64_t dst = static_cast<int64_t>(b.dst[blockIdx.x]) * tile_words;
+    const int64_t lo = static_cast<int64_t>(blockIdx.z) * per_split;
+    const int64_t hi = lo + per_split < tile_words ? lo + per_split : tile_words;
+    for (int64_t i = lo + threadIdx.x; i < hi; i += 256) pool[dst + i] = pool[src + i];
+}
+
+}  // namespace
+}  // namespace pa
+
+extern "C" {
+
+int pa_cache_write(void* k_cache, void* v_cache, const pa_cache_desc* desc, const void* k_new,
+                   const void* v_new, const int64_t* slot_mapping, int32_t num_tokens,
+                   void* stream) {
+    using namespace pa;
+    if (!desc_ok(desc) || num_tokens < 0) return PA_ERR_INVALID_ARG;
+    if (num_tokens == 0) return PA_OK;
+    if (!k_cache || !v_cache || !k_new || !v_new || !slot_mapping) return PA_ERR_INVALID_ARG;
+    if (desc->head_dim % 2) return PA_ERR_UNSUPPORTED;
+    const int32_t H = desc->num_kv_heads, D = desc->head_dim, bs = desc->block_size;
+    const int64_t num_slots = static_cast<int64_t>(desc->num_blocks) * bs;
+    const int E = desc->kv_dtype == PA_BF16 ? 2 : 1;
+    const int64_t total = static_cast<int64_t>(num_tokens) * H * (D / E);
+    const int64_t grid = (total + 255) / 256;
+    if (grid > INT32_MAX) return PA_ERR_UNSUPPORTED;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (desc->kv_dtype == PA_BF16) {
+        cache_write_kernel<uint16_t><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st>>>(
+            static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
+            static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), slot_mapping,
+            num_tokens, H, D, bs, num_slots);
+    } else {
+        cache_write_kernel<uint32_t><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st>>>(
+            static_cast<uint32_t*>(k_cache), static_cast<uint32_t*>(v_cache),
+            static_cast<const uint32_t*>(k_new), static_cast<const uint32_t*>(v_new), slot_mapping,
+            num_tokens, H, D, bs, num_slots);
+    }
+    return launch_status();
+}
+
+int pa_copy_blocks(void* k_cache, void* v_cache, const pa_cache_desc* desc,
+                   const int64_t* pairs_host, int32_t n_pairs, void* stream) {
+    using namespace pa;
+    if (!desc_ok(desc) || n_pairs < 0) return PA_ERR_INVALID_ARG;
+    if (n_pairs == 0) return PA_OK;
+    if (!k_cache || !v_cache || !pairs_host) return PA_ERR_INVALID_ARG;
+    const int64_t N = desc->num_blocks;
+    // Validate the whole list before launching anything: ids in range, no
+    // destination twice, no destination that is also a source (so the copies
+    // commute and may run concurrently).
+    for (int32_t i = 0; i < n_pairs; ++i) {
+        const int64_t s = pairs_host[2 * i], d = pairs_host[2 * i + 1];
+        if (s < 0 || s >= N || d < 0 || d >= N) return PA_ERR_INVALID_ARG;
+        for (int32_t k = 0; k < n_pairs; ++k) {
+            if (k != i && pairs_host[2 * k + 1] == d) return PA_ERR_INVALID_ARG;
+            if (pairs_host[2 * k] == d) return PA_ERR_INVALID_ARG;
+        }
+    }
+    const int64_t tile_bytes = static_cast<int64_t>(desc->num_kv_heads) * desc->block_size *
+                               desc->head_dim * static_cast<int64_t>(dtype_size(desc->kv_dtype));
+    if (tile_bytes % 16) return PA_ERR_UNSUPPORTED;
+    const int64_t tile_words = tile_bytes / 16;
+    const int64_t per_split = 256 * 4;                          // 16 KB per workgroup
+    const int64_t splits = (tile_words + per_split - 1) / per_split;
+    if (splits > 65535) return PA_ERR_UNSUPPORTED;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    for (int32_t base = 0; base < n_pairs; base += kPairsPerLaunch) {
+        const int32_t n = n_pairs - base < kPairsPerLaunch ? n_pairs - base : kPairsPerLaunch;
+        CopyBatch b{};
+        for (int32_t i = 0; i < n; ++i) {
+            b.src[i] = static_cast<int32_t>(pairs_host[2 * (base + i)]);
+            b.dst[i] = static_cast<int32_t>(pairs_host[2 * (base + i) + 1]);
+        }
+        copy_blocks_kernel<<<dim3(n, 2, static_cast<uint32_t>(splits)), dim3(256), 0, st>>>(
+            static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), b, tile_words, per_split);
+        const int rc = launch_status();
+        if (rc != PA_OK) return rc;
+    }
+    return PA_OK;
+}
+
+}  // extern "C"

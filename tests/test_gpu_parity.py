@@ -1,0 +1,242 @@
+"""GPU parity: the HIP library against the CPU oracle, through the C ABI.
+
+Bars: block tables, slots, copy-on-write pairs and whole pools (every byte,
+the NaN sentinel of never-written slots included) are bit-exact; attention
+outputs are within max abs error 1e-5 (fp32 cache) and 2e-2 (bf16 cache,
+fp32 accumulation), and additionally within the kernel's own error budget
+(2e-6 / 2e-4: fp32 logits and weights, the value pass fed a hi+lo bf16 split
+of each weight).  Probes with sharp structure (needles, one-hot and constant
+values) catch indexing mistakes that a flat softmax would hide under 2e-2.
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from tests import lib_run, oracle_run
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+BUDGET = {"f32": 2e-6, "bf16": 2e-4}
+
+SMALL = ["c1", "c2", "c3", "c4", "c4a", "c5"]
+
+
+def _announce(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module", params=SMALL)
+def case(request):
+    name = request.param
+    _announce(f"build {name} (small)")
+    w = workloads.make(name, small=True)
+    st_o = oracle_run.build(w)
+    st_l = lib_run.build(w)
+    torch.cuda.synchronize()
+    return name, w, st_o, st_l
+
+
+def test_tables_and_slots_bit_exact(case):
+    name, w, st_o, st_l = case
+    t_o, l_o = oracle_run.decode_tables(w, st_o)
+    assert np.array_equal(np.asarray(t_o, dtype=np.int32), st_l.tables_host)
+    assert np.array_equal(np.asarray(l_o, dtype=np.int32), st_l.lens_host)
+    assert [tuple(p) for p in st_o.step_pairs] == [tuple(p) for p in st_l.step_pairs]
+    assert np.array_equal(np.asarray(st_o.step_slots, dtype=np.int64), st_l.step_slots)
+
+
+def test_pools_bit_exact(case):
+    name, w, st_o, st_l = case
+    for dev, host in ((st_l.kc, st_o.kpool), (st_l.vc, st_o.vpool)):
+        got = lib_run.pool_bits(dev, w.dtype)
+        want = host.view(np.uint16 if w.dtype == "bf16" else np.uint32)
+        assert got.shape == want.shape
+        bad = np.flatnonzero(got != want)
+        assert bad.size == 0, f"{bad.size} elements differ, first at {bad[:5]}"
+
+
+def test_decode_matches_oracle(case):
+    name, w, st_o, st_l = case
+    _announce(f"decode {name}")
+    want = oracle_run.oracle_decode(w, st_o)
+    got = lib_run.decode(w, st_l).double().cpu().numpy()
+    err = np.max(np.abs(got - want))
+    assert np.isfinite(got).all()
+    assert err <= TOL[w.dtype], err
+    assert err <= BUDGET[w.dtype], err
+
+
+@pytest.mark.parametrize("part", [128, 256, 384])
+def test_partition_sizes(case, part):
+    name, w, st_o, st_l = case
+    want = oracle_run.oracle_decode(w, st_o)
+    got = lib_run.decode(w, st_l, partition_size=part).double().cpu().numpy()
+    assert np.max(np.abs(got - want)) <= BUDGET[w.dtype]
+
+
+def test_bf16_output(case):
+    name, w, st_o, st_l = case
+    want = oracle_run.oracle_decode(w, st_o)
+    got = lib_run.decode(w, st_l, out_dtype=torch.bfloat16).double().cpu().numpy()
+    # rounding the output to bf16 adds at most half an ulp of |out|
+    assert np.all(np.abs(got - want) <= BUDGET[w.dtype] + np.abs(want) * 2.0 ** -8)
+
+
+# ---- invariances: bit-identical outputs ----------------------------------------------
+def test_relabelled_blocks_bit_identical():
+    w = workloads.make("c2", small=True)
+    w2 = workloads.relayout(w, free_seed=1234)
+    a = lib_run.decode(w, lib_run.build(w))
+    st2 = lib_run.build(w2)
+    assert not np.array_equal(lib_run.build(w).tables_host, st2.tables_host)
+    b = lib_run.decode(w2, st2)
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("name", ["c4", "c4a"])
+def test_shared_prefix_bit_identical_to_duplicated(name):
+    w = workloads.make(name, small=True)
+    wd = workloads.relayout(w, duplicate_shared=True)
+    st = lib_run.build(w)
+    assert len(st.step_pairs) >= len(w.decode_seqs) - 1
+    a = lib_run.decode(w, st)
+    b = lib_run.decode(wd, lib_run.build(wd))
+    assert torch.equal(a, b)
+
+
+# ---- probes with sharp structure -------------------------------------------------------
+def _probe_workload(base, k=None, v=None, q=None):
+    return dataclasses.replace(base, k_tok=base.k_tok if k is None else k,
+                               v_tok=base.v_tok if v is None else v,
+                               q_dec=base.q_dec if q is None else q)
+
+
+def _bf16(x):
+    return workloads.round_to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+def _run_both(w):
+    st_o, st_l = oracle_run.build(w), lib_run.build(w)
+    return oracle_run.oracle_decode(w, st_o), lib_run.decode(w, st_l).double().cpu().numpy()
+
+
+def test_needle_in_every_logical_block():
+    base = workloads.make("c3", small=True)       # 2 x 3000 tokens, several partitions
+    bs, G, D = base.block_size, base.group, base.head_dim
+    q = np.zeros((2, base.num_q_heads, D), dtype=np.float32)
+    q[:, :, 0] = 1.0                               # every head looks along channel 0
+    k = np.zeros(base.k_tok.shape, dtype=np.float32)
+    v = np.zeros(base.v_tok.shape, dtype=np.float32)
+    # sequence s, kv head g: the needle sits in logical block (7*s + 3*g + 1) mod nblocks
+    needles = {}
+    for s in range(2):
+        rows = base.tok_rows[s]
+        nb = -(-len(rows) // bs)
+        for g in range(base.num_kv_heads):
+            blk = (7 * s + 3 * g + 1) % nb
+            pos = min(blk * bs + (g % bs), len(rows) - 1)
+            k[rows[pos], g, 0] = 200.0             # logit 200/sqrt(128) ~ 17.7 above all others
+            v[rows[pos], g, :] = np.arange(D) + 10 * g + 1000 * s
+            needles[(s, g)] = v[rows[pos], g, :].copy()
+    w = _probe_workload(base, k=_bf16(k), v=_bf16(v), q=_bf16(q))
+    want, got = _run_both(w)
+    assert np.max(np.abs(got - want)) <= 2e-4 * np.abs(want).max()
+    for (s, g), vec in needles.items():
+        for h in range(g * G, (g + 1) * G):
+            # weight of the needle >= 1 - L*exp(-17.7): the output is its value row
+            assert np.allclose(got[s, h], vec.astype(np.float64), rtol=0, atol=1e-2 * np.abs(vec).max())
+
+
+def test_constant_values_per_kv_head_and_ones():
+    base = workloads.make("c2", small=True)
+    v = np.empty(base.v_tok.shape, dtype=np.float32)
+    for g in range(base.num_kv_heads):
+        v[:, g, :] = g + 1.0
+    w = _probe_workload(base, v=_bf16(v))
+    _, got = _run_both(w)
+    for h in range(base.num_q_heads):
+        # the weights sum to one; the hi+lo split keeps each to 2^-18 relative
+        c = h // base.group + 1.0
+        assert np.max(np.abs(got[:, h, :] / c - 1.0)) <= 1e-5
+
+
+def test_one_hot_values_give_the_weights():
+    base = workloads.make("c1")                    # L <= 48 <= D = 64
+    v = np.zeros(base.v_tok.shape, dtype=np.float32)
+    for s in base.decode_seqs:
+        for pos, row in enumerate(base.tok_rows[s]):
+            v[row, :, pos] = 1.0
+    w = _probe_workload(base, v=v)
+    st_o, st_l = oracle_run.build(w), lib_run.build(w)
+    got = lib_run.decode(w, st_l).double().cpu().numpy()
+    from oracle import attention
+    tables, lens = oracle_run.decode_tables(w, st_o)
+    q = attention.stored_to_f64(w.q_dec, w.dtype)
+    for i, s in enumerate(w.decode_seqs):
+        for h in range(w.num_q_heads):
+            wts = attention.decode_weights(q[i, h], st_o.kpool, st_o.vpool, w.dtype, w.num_kv_heads,
+                                           w.block_size, w.head_dim, tables[i], lens[i], h // w.group,
+                                           w.scale)
+            assert np.max(np.abs(got[i, h, :lens[i]] - wts)) <= 1e-6
+            assert np.all(got[i, h, lens[i]:] == 0.0)
+
+
+def test_length_one_returns_v_exactly():
+    rng = np.random.default_rng(9)
+    w = workloads.configs._decode_batch_from(rng, "len1", "bf16", [1, 1, 2, 1, 513], 32, 8, 128, 16)
+    st_l = lib_run.build(w)
+    got = lib_run.decode(w, st_l).cpu().numpy()
+    for i, s in enumerate(w.decode_seqs):
+        if w.seq_len(s) != 1:
+            continue
+        row = w.tok_rows[s][0]
+        vref = (w.v_tok[row].astype(np.uint32) << 16).view(np.float32)   # [Hkv, D]
+        for h in range(w.num_q_heads):
+            assert np.array_equal(got[i, h], vref[h // w.group])
+
+
+# ---- edge cases ------------------------------------------------------------------------------
+def test_invalid_rows_give_nan_and_leave_others_alone():
+    w = workloads.make("c2", small=True)
+    st = lib_run.build(w)
+    good = lib_run.decode(w, st)
+    lens = st.lens.clone()
+    lens[1] = 0                                   # invalid length
+    lens[2] = st.max_ctx + 1                      # beyond the declared maximum
+    tables = st.tables.clone()
+    tables[3, 0] = w.num_blocks                   # out-of-range block id
+    tables[4, 1] = -7
+    out = lib_run.decode(w, st, lens=lens, tables=tables)
+    for i in (1, 2, 3, 4):
+        assert torch.isnan(out[i]).all(), i
+    keep = [i for i in range(len(w.decode_seqs)) if i not in (1, 2, 3, 4)]
+    assert torch.equal(out[keep], good[keep])
+
+
+def test_empty_batch_is_a_no_op():
+    import paged_kv_cache_424_amd as pa
+    w = workloads.make("c1")
+    st = lib_run.build(w)
+    q = st.q[:0]
+    out = torch.empty((0, w.num_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    pa.pa_decode(out, q, st.kc, st.vc, st.desc, st.tables[:0], st.lens[:0], 1, w.scale)
+    pa.pa_cache_write(st.kc, st.vc, st.desc, q[:0, :w.num_kv_heads], q[:0, :w.num_kv_heads],
+                      torch.empty(0, dtype=torch.int64, device="cuda"))
+    pa.pa_copy_blocks(st.kc, st.vc, st.desc, [])
+    torch.cuda.synchronize()
+
+
+def test_negative_slots_are_padding():
+    import paged_kv_cache_424_amd as pa
+    w = workloads.make("c1")
+    st = lib_run.build(w)
+    before_k = lib_run.pool_bits(st.kc, w.dtype).copy()
+    k = torch.randn((3, w.num_kv_heads, w.head_dim), device="cuda")
+    slots = torch.tensor([-1, -5, -100], dtype=torch.int64, device="cuda")
+    pa.pa_cache_write(st.kc, st.vc, st.desc, k, k, slots)
+    assert np.array_equal(before_k, lib_run.pool_bits(st.kc, w.dtype))
