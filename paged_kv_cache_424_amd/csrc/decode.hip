@@ -107,7 +107,8 @@ struct ChunkRegs {
 };
 
 template <bool BF16, int D, int NCH>
-__global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void decode_partition_kernel(
+    DecodeArgs a) {
     constexpr int PART = kChunk * kWaves * NCH;
     constexpr int ES = BF16 ? 2 : 4;
     using Regs = ChunkRegs<BF16, D>;
@@ -183,39 +184,37 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
 
     const int part0 = p * PART;                   // first absolute position of the partition
 
+    // Loads are unconditional: every address is inside the pool (ids of blocks
+    // past the sequence's end were replaced by block 0 above), so no load sits
+    // behind a divergent branch and all of a chunk's loads issue back to back.
+    // Rows past the context end are dealt with when the chunk is consumed: their
+    // logits are selected to -inf and their values to 0.
     auto load_chunk = [&](int ci, Regs& R) {
         const int tc = ci * kChunk;               // chunk offset inside the partition
         // K: row r of tile t is chunk token 8*(r>>2) + (r&3) + 4t.
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const int tp = tc + 8 * (r >> 2) + (r & 3) + 4 * t;
-            const bool ok = part0 + tp < L;
             const int64_t blk = s_blk[tp / bs];
             const char* row = kbase + ((blk * tile_elems) + static_cast<int64_t>(tp % bs) * D) * ES;
 #pragma unroll
             for (int c = 0; c < Regs::KV; ++c) {
                 const int d0 = BF16 ? c * 32 + j * 8 : j * (D / 4) + 4 * c;
-                R.k[t][c] = ok ? ldg_nt(row + static_cast<int64_t>(d0) * ES) : kZero4;
+                R.k[t][c] = ldg_nt(row + static_cast<int64_t>(d0) * ES);
             }
         }
         // V: lane (j, r) reads tokens 8j..8j+7 of channel mt*16 + r.
         const int tp0 = tc + 8 * j;
-        const int nvalid = L - (part0 + tp0);
         const int64_t blk = s_blk[tp0 / bs];
-        const int off = tp0 % bs;
-        const char* vb = vbase + (blk * tile_elems + off) * ES;
+        const char* vb = vbase + (blk * tile_elems + tp0 % bs) * ES;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             const int64_t ch = mt * 16 + r;
             if (BF16) {
-                const u32x4 x = nvalid > 0 ? ldg_nt(vb + ch * bs * ES) : kZero4;
-                R.v[mt] = nvalid >= 8 ? x : keep_first_bf16(x, nvalid);
+                R.v[mt] = ldg_nt(vb + ch * bs * ES);
             } else {
-                const char* pv = vb + ch * bs * ES;
-                const u32x4 x0 = nvalid > 0 ? ldg_nt(pv) : kZero4;
-                const u32x4 x1 = nvalid > 4 ? ldg_nt(pv + 16) : kZero4;
-                R.v[2 * mt] = nvalid >= 4 ? x0 : keep_first_f32(x0, nvalid);
-                R.v[2 * mt + 1] = nvalid >= 8 ? x1 : keep_first_f32(x1, nvalid - 4);
+                R.v[2 * mt] = ldg_nt(vb + ch * bs * ES);
+                R.v[2 * mt + 1] = ldg_nt(vb + ch * bs * ES + 16);
             }
         }
     };
@@ -278,6 +277,18 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
         // ---- values: O^T[channel][head] += V^T[channel][token] . P^T ----
+        // A weight of 0 does not cancel a NaN value (never-written slots past
+        // the context end), so those values are zeroed by select.
+        Regs Rm = R;
+        if (part0 + tc + kChunk > L) {
+#pragma unroll
+            for (int x = 0; x < Regs::VV; ++x) {
+                if constexpr (BF16)
+                    Rm.v[x] = keep_first_bf16(R.v[x], ntok);
+                else
+                    Rm.v[x] = keep_first_f32(R.v[x], (x & 1) ? ntok - 4 : ntok);
+            }
+        }
         if constexpr (BF16) {
             bf16x8_t ph, pl;
 #pragma unroll
@@ -288,13 +299,13 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
             }
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.v[mt]), ph, acc[mt], 0, 0, 0);
-                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.v[mt]), pl, acc[mt], 0, 0, 0);
+                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Rm.v[mt]), ph, acc[mt], 0, 0, 0);
+                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Rm.v[mt]), pl, acc[mt], 0, 0, 0);
             }
         } else {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const u32x4 v0 = R.v[2 * mt], v1 = R.v[2 * mt + 1];
+                const u32x4 v0 = Rm.v[2 * mt], v1 = Rm.v[2 * mt + 1];
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
                     acc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(e < 4 ? v0[e] : v1[e - 4]), pv[e],
@@ -303,18 +314,21 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
         }
     };
 
-    // Software pipeline over this wave's chunks: load chunk k+1 while chunk k computes.
-    Regs R0, R1;
+    // Chunk loop.  Latency is hidden by occupancy, not by an explicit register
+    // double buffer: the kernel is held to >= 3 waves per SIMD (at most ~168
+    // registers each), which leaves the scheduler room to start a chunk's
+    // sixteen 16-byte loads early while keeping three workgroups resident per
+    // CU -- one workgroup's start-up (length, block ids, query) and merge then
+    // overlap the others' streaming.  An explicit two-chunk buffer needs ~260
+    // registers and one wave per SIMD, and measured 25 % slower.
     const int first_empty = (L - part0 + kChunk - 1) / kChunk;   // chunks >= this are empty
-    if (w < first_empty) load_chunk(w, R0);
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
         const int ci = w + kWaves * k;
         if (ci >= first_empty) break;
-        Regs& cur = (k & 1) ? R1 : R0;
-        Regs& nxt = (k & 1) ? R0 : R1;
-        if (k + 1 < NCH && ci + kWaves < first_empty) load_chunk(ci + kWaves, nxt);
-        compute_chunk(ci, cur);
+        Regs R;
+        load_chunk(ci, R);
+        compute_chunk(ci, R);
     }
 
     // ---- merge the four waves through LDS ----
@@ -361,43 +375,81 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
     }
 }
 
-// One wave per (sequence, query head): merge the partitions of sequences that
-// have more than one.  With M the largest partition max, each partition's sum
-// and output are weighted by 2^(m_p - M); the output is their ratio.  The sum
-// over partitions runs in partition order.
+// One workgroup per (sequence, query head): merge the partitions of a
+// sequence that has more than one.  With M the largest partition max, each
+// partition's sum and output are weighted by 2^(m_p - M); the result is their
+// ratio.  Thread t owns channel t % D and the partitions p = t / D (mod 256/D);
+// the partial sums are combined through LDS in a fixed order, so the result
+// does not depend on timing.
+__device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const float o = __shfl_xor(v, off);
+        v = is_max ? fmaxf(v, o) : v + o;
+    }
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    float r = red[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) r = is_max ? fmaxf(r, red[i]) : r + red[i];
+    return r;
+}
+
 __global__ __launch_bounds__(256) void decode_reduce_kernel(void* out, int out_bf16,
                                                            const int32_t* __restrict__ lens,
                                                            const float* __restrict__ ws_acc,
                                                            const float2* __restrict__ ws_ml, int32_t B,
                                                            int32_t Hq, int32_t D, int32_t max_ctx,
                                                            int32_t part, int32_t P) {
-    const int pair = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (pair >= B * Hq) return;
-    const int lane = threadIdx.x & 63;
+    const int pair = blockIdx.x;
     const int s = pair / Hq;
     const int L = lens[s];
     if (L < 1 || L > max_ctx) return;                       // the partition kernel wrote NaN
     const int np = (L + part - 1) / part;
     if (np <= 1) return;                                    // already final
+    __shared__ float red[4];
+    __shared__ float s_part[256];
+    const int tid = threadIdx.x;
     const float2* ml = ws_ml + static_cast<int64_t>(pair) * P;
-    float M = -INFINITY;
-    for (int i = lane; i < np; i += 64) M = fmaxf(M, ml[i].x);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    float den = 0.f;
-    for (int i = 0; i < np; ++i) {
+    float m = -INFINITY;
+    for (int i = tid; i < np; i += 256) m = fmaxf(m, ml[i].x);
+    const float M = block_reduce(m, red, true);
+    float dp = 0.f;
+    for (int i = tid; i < np; i += 256) {
         const float2 v = ml[i];
-        den += __builtin_amdgcn_exp2f(v.x - M) * v.y;
+        dp += __builtin_amdgcn_exp2f(v.x - M) * v.y;
     }
-    const float* accp = ws_acc + static_cast<int64_t>(pair) * P * D;
-    for (int d = lane; d < D; d += 64) {
-        float o = 0.f;
-        for (int i = 0; i < np; ++i) o += __builtin_amdgcn_exp2f(ml[i].x - M) * accp[static_cast<int64_t>(i) * D + d];
+    const float den = block_reduce(dp, red, false);
+
+    const int groups = 256 / D;                             // D divides 256
+    const int d = tid % D, grp = tid / D;
+    const float* accp = ws_acc + static_cast<int64_t>(pair) * P * D + d;
+    // four independent partial sums keep four loads in flight per thread
+    float o[4] = {0.f, 0.f, 0.f, 0.f};
+    int i = grp;
+    for (; i + 3 * groups < np; i += 4 * groups) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int pi = i + u * groups;
+            o[u] += __builtin_amdgcn_exp2f(ml[pi].x - M) * accp[static_cast<int64_t>(pi) * D];
+        }
+    }
+    for (int u = 0; i < np; i += groups, ++u)
+        o[u] += __builtin_amdgcn_exp2f(ml[i].x - M) * accp[static_cast<int64_t>(i) * D];
+    const float o0 = o[0] + o[2], o1 = o[1] + o[3];
+    s_part[tid] = o0 + o1;
+    __syncthreads();
+    if (grp == 0) {
+        float o = s_part[d];
+        for (int g2 = 1; g2 < groups; ++g2) o += s_part[g2 * D + d];
         const float v = o / den;
+        const int64_t idx = static_cast<int64_t>(pair) * D + d;
         if (out_bf16)
-            static_cast<__bf16*>(out)[static_cast<int64_t>(pair) * D + d] = static_cast<__bf16>(v);
+            static_cast<__bf16*>(out)[idx] = static_cast<__bf16>(v);
         else
-            static_cast<float*>(out)[static_cast<int64_t>(pair) * D + d] = v;
+            static_cast<float*>(out)[idx] = v;
     }
 }
 
@@ -533,7 +585,7 @@ int pa_decode_reduce(void* out, int32_t out_dtype, const int32_t* context_lens, 
     const float* ws_acc = static_cast<const float*>(workspace);
     const float2* ws_ml =
         reinterpret_cast<const float2*>(static_cast<const char*>(workspace) + (acc_bytes + 255) / 256 * 256);
-    const int64_t grid = (pairs + 3) / 4;
+    const int64_t grid = pairs;
     if (grid > INT32_MAX) return PA_ERR_UNSUPPORTED;
     decode_reduce_kernel<<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
         out, out_dtype == PA_BF16, context_lens, ws_acc, ws_ml, num_seqs, num_q_heads, head_dim,

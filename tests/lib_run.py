@@ -58,14 +58,14 @@ def run_script(w, alloc):
 
 def _write(st, w, items, device):
     if not items:
-        return
+        return np.empty(0, dtype=np.int64), np.empty(0, dtype=np.int64)
     slots = np.concatenate([s for s, _ in items]).astype(np.int64)
     rows = np.concatenate([r for _, r in items])
     k = torch_stored(w.k_tok[rows], w.dtype).to(device)
     v = torch_stored(w.v_tok[rows], w.dtype).to(device)
     sl = torch.from_numpy(slots).to(device)
     pa.pa_cache_write(st.kc, st.vc, st.desc, k, v, sl)
-    return slots
+    return slots, rows
 
 
 def build(w, device="cuda", run_step=True):
@@ -87,7 +87,7 @@ def build(w, device="cuda", run_step=True):
     if run_step:
         if st.step_pairs:
             pa.pa_copy_blocks(st.kc, st.vc, st.desc, st.step_pairs)
-        st.step_slots = _write(st, w, writes["step"], device)
+        st.step_slots, st.step_rows = _write(st, w, writes["step"], device)
     st.max_blocks = max(-(-len(r) // w.block_size) for r in w.tok_rows.values())
     tables, lens = pa.pa_build_block_tables(st.alloc, w.decode_seqs, st.max_blocks)
     st.tables_host, st.lens_host = tables, lens

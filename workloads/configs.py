@@ -296,3 +296,18 @@ def relayout(w, block_size=None, free_seed=None, duplicate_shared=False):
                     decode_seqs=w.decode_seqs, q_dec=w.q_dec, prefill_seqs=w.prefill_seqs,
                     chunk_len=w.chunk_len, q_pre=w.q_pre, partition_size=w.partition_size,
                     note=w.note + " (relayout)")
+
+
+def subset(w, seqs):
+    """A workload holding only the listed decode sequences (same K/V rows and
+    queries), each stored privately in a fresh pool -- a bounded sample of w."""
+    seqs = list(seqs)
+    idx = [w.decode_seqs.index(s) for s in seqs]
+    tok_rows = {i: w.tok_rows[s] for i, s in enumerate(seqs)}
+    sub = Workload(name=w.name + "-subset", dtype=w.dtype, num_q_heads=w.num_q_heads,
+                   num_kv_heads=w.num_kv_heads, head_dim=w.head_dim, block_size=w.block_size,
+                   num_blocks=1, free_order=np.zeros(1, dtype=np.int32), scale=w.scale,
+                   script=[], tok_rows=tok_rows, k_tok=w.k_tok, v_tok=w.v_tok,
+                   decode_seqs=list(range(len(seqs))), q_dec=w.q_dec[idx],
+                   partition_size=w.partition_size, note=w.note + f" (sequences {seqs})")
+    return relayout(sub, duplicate_shared=True, free_seed=7)
