@@ -230,6 +230,34 @@ int pa_decode_reduce(void* out, int32_t out_dtype, const int32_t* context_lens, 
                      int32_t partition_size, void* workspace, size_t workspace_bytes,
                      void* stream);
 
+/* Causal attention of prefill chunks over their paged context, the prefill half
+ * of a continuous-batching step ([studynote 223] section IV checklist item 2;
+ * [studynote 528] section II, continuous batching table).
+ *   q:                device [num_query_tokens][num_q_heads][head_dim] (cache dtype),
+ *                     the queries of all chunks back to back; chunk c owns rows
+ *                     query_start_loc[c] .. query_start_loc[c+1]-1.
+ *   query_start_loc:  device int32 [num_chunks+1], non-decreasing, within
+ *                     [0, num_query_tokens].
+ *   context_lens:     device int32 [num_chunks]; L_c counts the chunk's own tokens,
+ *                     which must already be in the cache as its last C_c positions.
+ *                     Query i of the chunk sits at position L_c - C_c + i and sees
+ *                     positions 0..L_c - C_c + i.
+ *   block_tables:     device int32 [num_chunks][max_blocks_per_seq].
+ *   max_query_len:    upper bound of every C_c (grid sizing).
+ *   out:              device [num_query_tokens][num_q_heads][head_dim] of out_dtype;
+ *                     rows that belong to no chunk are not written.
+ * Device-side checks: the rows of a chunk with C_c < 0, C_c > max_query_len,
+ * L_c < C_c, L_c > max_blocks_per_seq*block_size or a needed table entry
+ * outside [0, num_blocks) are set to NaN (when they lie inside the output), and
+ * nothing is read out of bounds.  Supported: bf16 cache, head_dim 128,
+ * num_q_heads/num_kv_heads a power of two up to 16, block_size 8..256 a power
+ * of two.  The value pass takes the softmax weights in bf16 (fp32 accumulate). */
+int pa_prefill(void* out, int32_t out_dtype, const void* q, const void* k_cache,
+               const void* v_cache, const pa_cache_desc* desc, const int32_t* block_tables,
+               int32_t max_blocks_per_seq, const int32_t* context_lens,
+               const int32_t* query_start_loc, int32_t num_chunks, int32_t num_query_tokens,
+               int32_t num_q_heads, int32_t max_query_len, float scale, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libpa.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is not built; run `python -m paged_kv_cache_424_amd.build` "
+        f"{LIB_PATH} is not built; run `python paged_kv_cache_424_amd/build.py` "
         "(there is no fallback implementation)")
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -91,10 +91,8 @@ _DEC = [_vp, _i32, _vp, _vp, _vp, _PD, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _
 _sig("pa_decode", ctypes.c_int, *_DEC)
 _sig("pa_decode_partitions", ctypes.c_int, *_DEC)
 _sig("pa_decode_reduce", ctypes.c_int, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp)
-_HAS_PREFILL = hasattr(_lib, "pa_prefill")
-if _HAS_PREFILL:
-    _sig("pa_prefill", ctypes.c_int, _vp, _i32, _vp, _vp, _vp, _PD, _vp, _i32, _vp, _vp, _i32,
-         _i32, _i32, _f32, _vp)
+_sig("pa_prefill", ctypes.c_int, _vp, _i32, _vp, _vp, _vp, _PD, _vp, _i32, _vp, _vp, _i32, _i32,
+     _i32, _i32, _f32, _vp)
 
 
 def _check(rc, where):
@@ -314,11 +312,10 @@ def pa_decode_reduce(out, context_lens, num_q_heads, head_dim, max_context_len, 
 
 def pa_prefill(out, q, k_cache, v_cache, desc, block_tables, context_lens, query_start_loc,
                max_query_len, scale, stream=None):
-    if not _HAS_PREFILL:
-        raise PAError(PA_ERR_UNSUPPORTED, "pa_prefill")
     _check(_lib.pa_prefill(_dev(out, "out"), _out_dtype(out), _dev(q, "q"), _dev(k_cache, "k_cache"),
                            _dev(v_cache, "v_cache"), ctypes.byref(desc), _dev(block_tables, "block_tables"),
                            int(block_tables.shape[1]), _dev(context_lens, "context_lens"),
                            _dev(query_start_loc, "query_start_loc"), int(context_lens.numel()),
-                           int(q.shape[1]), int(max_query_len), float(scale), _stream(stream)),
+                           int(q.shape[0]), int(q.shape[1]), int(max_query_len), float(scale),
+                           _stream(stream)),
            "pa_prefill")

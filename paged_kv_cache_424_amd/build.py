@@ -1,6 +1,8 @@
 """Build the HIP library libpa.so in-tree for gfx950.
 
-    python -m paged_kv_cache_424_amd.build
+    python paged_kv_cache_424_amd/build.py
+
+(run it as a script: importing the package first would load the old library)
 
 Host-only C++ (allocator, layout) is compiled with g++; the HIP sources with
 hipcc --offload-arch=gfx950.  Packed-fp32 instruction selection is turned off

@@ -118,3 +118,18 @@ def pool_bits(t, dtype):
     if dtype == "bf16":
         return t.view(torch.int16).cpu().numpy().view(np.uint16)
     return t.view(torch.int32).cpu().numpy().view(np.uint32)
+
+
+def prefill(w, st, out_dtype=torch.float32, lens=None, qsl=None, max_query_len=None):
+    """Run pa_prefill for the workload's prefill chunks (after build())."""
+    dev = st.kc.device
+    tables, clens = pa.pa_build_block_tables(st.alloc, w.prefill_seqs, st.max_blocks)
+    tab = torch.from_numpy(np.ascontiguousarray(tables)).to(dev)
+    lens = torch.from_numpy(np.ascontiguousarray(clens)).to(dev) if lens is None else lens
+    if qsl is None:
+        qsl = torch.from_numpy(np.concatenate([[0], np.cumsum(w.chunk_len)]).astype(np.int32)).to(dev)
+    q = torch_stored(w.q_pre, w.dtype).to(dev)
+    out = torch.full((q.shape[0], q.shape[1], q.shape[2]), float("inf"), dtype=out_dtype, device=dev)
+    mq = max(w.chunk_len) if max_query_len is None else max_query_len
+    pa.pa_prefill(out, q, st.kc, st.vc, st.desc, tab, lens, qsl, mq, w.scale)
+    return out
