@@ -73,6 +73,13 @@ const char* pa_status_string(int status);
 /* ABI version of this header: (major << 16) | minor. */
 int32_t pa_version(void);
 
+/* The hipError_t value behind the most recent PA_ERR_HIP returned on the
+ * calling thread (hipSuccess = 0 if there was none), and its name as HIP
+ * spells it (static storage).  Launches are checked through their own return
+ * code, so an error left pending by unrelated HIP calls is never reported. */
+int32_t pa_last_hip_error(void);
+const char* pa_last_hip_error_name(void);
+
 /* ---- layout (host) ----------------------------------------------------------- */
 
 /* Bytes of ONE pool (K or V) for this shape; 0 if desc is invalid. */

@@ -10,6 +10,11 @@ import ctypes
 import os
 
 import numpy as np
+# torch is imported before the library is loaded.  torch ships its own HIP
+# runtime (libamdhip64), whose soname the library's dependency matches, so the
+# library then binds to that same runtime.  Loaded the other way round, the
+# process would hold two HIP runtimes and the library's one sees no device.
+import torch  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpa.so")
@@ -20,6 +25,20 @@ if not os.path.exists(LIB_PATH):
         "(there is no fallback implementation)")
 
 _lib = ctypes.CDLL(LIB_PATH)
+
+
+def _hip_runtimes():
+    """Paths of the HIP runtime libraries mapped into this process."""
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({line.split()[-1] for line in f if "libamdhip64" in line})
+    except OSError:                                   # pragma: no cover
+        return []
+
+
+if len(_hip_runtimes()) > 1:
+    raise ImportError("more than one HIP runtime is loaded in this process "
+                      f"({_hip_runtimes()}); load torch before any other HIP library")
 
 PA_OK = 0
 PA_ERR_INVALID_ARG = -1
@@ -37,7 +56,10 @@ PA_BF16 = 1
 class PAError(RuntimeError):
     def __init__(self, status, where):
         self.status = status
-        super().__init__(f"{where}: {pa_status_string(status)} ({status})")
+        msg = f"{where}: {pa_status_string(status)} ({status})"
+        if status == PA_ERR_HIP:
+            msg += f" [{pa_last_hip_error_name()} = {pa_last_hip_error()}]"
+        super().__init__(msg)
 
 
 class pa_cache_desc(ctypes.Structure):
@@ -68,6 +90,8 @@ def _sig(name, res, *args):
 
 _lib_status_string = _sig("pa_status_string", ctypes.c_char_p, ctypes.c_int)
 _sig("pa_version", _i32)
+_sig("pa_last_hip_error", _i32)
+_sig("pa_last_hip_error_name", ctypes.c_char_p)
 _sig("pa_cache_pool_bytes", _sz, _PD)
 _sig("pa_kv_offset", _i64, _PD, _i32, _i64, _i32, _i32)
 _sig("pa_allocator_create", ctypes.c_int, _i32, _i32, _P32, ctypes.POINTER(_vp))
@@ -115,6 +139,14 @@ def pa_status_string(status):
 
 def pa_version():
     return _lib.pa_version()
+
+
+def pa_last_hip_error():
+    return _lib.pa_last_hip_error()
+
+
+def pa_last_hip_error_name():
+    return _lib.pa_last_hip_error_name().decode()
 
 
 def pa_cache_pool_bytes(desc):

@@ -87,18 +87,16 @@ int pa_cache_write(void* k_cache, void* v_cache, const pa_cache_desc* desc, cons
     const int64_t grid = (total + 255) / 256;
     if (grid > INT32_MAX) return PA_ERR_UNSUPPORTED;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (desc->kv_dtype == PA_BF16) {
-        cache_write_kernel<uint16_t><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st>>>(
-            static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
-            static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), slot_mapping,
-            num_tokens, H, D, bs, num_slots);
-    } else {
-        cache_write_kernel<uint32_t><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st>>>(
-            static_cast<uint32_t*>(k_cache), static_cast<uint32_t*>(v_cache),
-            static_cast<const uint32_t*>(k_new), static_cast<const uint32_t*>(v_new), slot_mapping,
-            num_tokens, H, D, bs, num_slots);
-    }
-    return launch_status();
+    const dim3 g(static_cast<uint32_t>(grid));
+    if (desc->kv_dtype == PA_BF16)
+        return launch_kernel(cache_write_kernel<uint16_t>, g, dim3(256), 0, st,
+                             static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
+                             static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+                             slot_mapping, num_tokens, H, D, bs, num_slots);
+    return launch_kernel(cache_write_kernel<uint32_t>, g, dim3(256), 0, st,
+                         static_cast<uint32_t*>(k_cache), static_cast<uint32_t*>(v_cache),
+                         static_cast<const uint32_t*>(k_new), static_cast<const uint32_t*>(v_new),
+                         slot_mapping, num_tokens, H, D, bs, num_slots);
 }
 
 int pa_copy_blocks(void* k_cache, void* v_cache, const pa_cache_desc* desc,
@@ -134,9 +132,9 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const pa_cache_desc* desc,
             b.src[i] = static_cast<int32_t>(pairs_host[2 * (base + i)]);
             b.dst[i] = static_cast<int32_t>(pairs_host[2 * (base + i) + 1]);
         }
-        copy_blocks_kernel<<<dim3(n, 2, static_cast<uint32_t>(splits)), dim3(256), 0, st>>>(
-            static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), b, tile_words, per_split);
-        const int rc = launch_status();
+        const int rc = launch_kernel(copy_blocks_kernel, dim3(n, 2, static_cast<uint32_t>(splits)),
+                                     dim3(256), 0, st, static_cast<uint4*>(k_cache),
+                                     static_cast<uint4*>(v_cache), b, tile_words, per_split);
         if (rc != PA_OK) return rc;
     }
     return PA_OK;

@@ -493,13 +493,12 @@ size_t workspace_bytes(int64_t B, int64_t Hq, int64_t D, int64_t P) {
 template <bool BF16, int D>
 int launch_partitions_nch(int nch, dim3 grid, size_t lds, hipStream_t st, const DecodeArgs& a) {
     switch (nch) {
-        case 1: decode_partition_kernel<BF16, D, 1><<<grid, dim3(kThreads), lds, st>>>(a); break;
-        case 2: decode_partition_kernel<BF16, D, 2><<<grid, dim3(kThreads), lds, st>>>(a); break;
-        case 3: decode_partition_kernel<BF16, D, 3><<<grid, dim3(kThreads), lds, st>>>(a); break;
-        case 4: decode_partition_kernel<BF16, D, 4><<<grid, dim3(kThreads), lds, st>>>(a); break;
+        case 1: return launch_kernel(decode_partition_kernel<BF16, D, 1>, grid, dim3(kThreads), lds, st, a);
+        case 2: return launch_kernel(decode_partition_kernel<BF16, D, 2>, grid, dim3(kThreads), lds, st, a);
+        case 3: return launch_kernel(decode_partition_kernel<BF16, D, 3>, grid, dim3(kThreads), lds, st, a);
+        case 4: return launch_kernel(decode_partition_kernel<BF16, D, 4>, grid, dim3(kThreads), lds, st, a);
         default: return PA_ERR_UNSUPPORTED;
     }
-    return launch_status();
 }
 
 }  // namespace
@@ -587,10 +586,9 @@ int pa_decode_reduce(void* out, int32_t out_dtype, const int32_t* context_lens, 
         reinterpret_cast<const float2*>(static_cast<const char*>(workspace) + (acc_bytes + 255) / 256 * 256);
     const int64_t grid = pairs;
     if (grid > INT32_MAX) return PA_ERR_UNSUPPORTED;
-    decode_reduce_kernel<<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
-        out, out_dtype == PA_BF16, context_lens, ws_acc, ws_ml, num_seqs, num_q_heads, head_dim,
-        max_context_len, part, P);
-    return launch_status();
+    return launch_kernel(decode_reduce_kernel, dim3(static_cast<uint32_t>(grid)), dim3(256), 0,
+                         static_cast<hipStream_t>(stream), out, out_dtype == PA_BF16, context_lens,
+                         ws_acc, ws_ml, num_seqs, num_q_heads, head_dim, max_context_len, part, P);
 }
 
 int pa_decode(void* out, int32_t out_dtype, const void* q, const void* k_cache, const void* v_cache,

@@ -5,6 +5,7 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <tuple>
 
 #include "../../include/pa.h"
 
@@ -20,10 +21,31 @@ inline bool desc_ok(const pa_cache_desc* d) {
            d->head_dim > 0 && dtype_size(d->kv_dtype) != 0;
 }
 
-inline int hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+// Remember a failed HIP call's error code for pa_last_hip_error() (per thread)
+// and return PA_ERR_HIP.  Defined in status.hip.
+int record_hip_error(hipError_t e);
 
-// Launch-error check after a kernel launch (does not synchronize).
-inline int launch_status() { return hip_status(hipGetLastError()); }
+inline int hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : record_hip_error(e); }
+
+// Launch `kernel` and return the status of that launch alone.  The launch's
+// own return code is used, never hipGetLastError(): the latter also reports
+// errors left behind by unrelated HIP calls of the host program.  Arguments
+// are converted to the kernel's parameter types first.  Does not synchronize.
+template <typename... KArgs, typename... Args>
+int launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds, hipStream_t st,
+                  Args... args) {
+    static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count");
+    std::tuple<KArgs...> vals(static_cast<KArgs>(args)...);
+    void* ptrs[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1] = {};
+    std::apply(
+        [&ptrs](auto&... v) {
+            int i = 0;
+            ((ptrs[i++] = const_cast<void*>(static_cast<const void*>(&v))), ...);
+        },
+        vals);
+    return hip_status(
+        hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, lds, st));
+}
 
 constexpr int kNumXcds = 8;   // MI355X: 8 XCDs, workgroups dispatched round-robin over them
 

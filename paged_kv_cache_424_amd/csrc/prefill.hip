@@ -349,6 +349,6 @@ extern "C" int pa_prefill(void* out, int32_t out_dtype, const void* q, const voi
     a.total_q = num_query_tokens;
     a.scale_log2 = scale * kLog2e;
     a.out_bf16 = out_dtype == PA_BF16;
-    prefill_kernel<<<dim3(static_cast<uint32_t>(units)), dim3(kThreads), 0, static_cast<hipStream_t>(stream)>>>(a);
-    return launch_status();
+    return launch_kernel(prefill_kernel, dim3(static_cast<uint32_t>(units)), dim3(kThreads), 0,
+                         static_cast<hipStream_t>(stream), a);
 }

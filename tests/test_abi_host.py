@@ -14,6 +14,7 @@ import os
 import random
 import re
 import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -44,6 +45,18 @@ def test_every_declared_function_is_exported():
     lib = ctypes.CDLL(pa.LIB_PATH)
     for n in names:
         assert getattr(lib, n) is not None
+
+
+def test_one_hip_runtime_when_the_package_is_imported_first():
+    # Importing the package before torch once left two HIP runtimes in the
+    # process (the library's from /opt/rocm, torch's own), and every launch
+    # then failed with hipErrorNoDevice.  The binding loads torch first.
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "import paged_kv_cache_424_amd as pa\n"
+            "from paged_kv_cache_424_amd import _binding\n"
+            "print(len(_binding._hip_runtimes()))\n" % ROOT)
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, check=True)
+    assert out.stdout.strip() == "1", out.stdout + out.stderr
 
 
 def test_status_strings_and_version():
