@@ -1,22 +1,38 @@
 #!/usr/bin/env python3
 """Paged decode attention throughput on one MI355X.
 
-A step is one pass of the decode hot path over one batch: the cache write of
-every sequence's new token, then the split-K partition kernel, then the
-rescaling reduce (plus the copy-on-write copies for the shared-prefix
-workload).  Inputs are resident in HBM before timing starts.  Prints one
-JSON line.
+A step is one pass of the hot path over one batch, with every input already
+resident in HBM:
 
-    python bench.py [--steps K] [--warmup W] [--workload c3|c2|c4]
+1. the copy-on-write block copies, when the workload has shared prefixes;
+2. the cache write of every token the step appends;
+3. the split-K decode partition kernel, then the rescaling reduce;
+4. for the mixed continuous-batching workload, the prefill-chunk kernel.
 
-Default workload: long-context decode, 8 sequences x 32768 tokens, 32 query /
-8 kv heads, head_dim 128, bf16 cache in 16-token blocks, 512-token
-partitions, keys scaled x3.  Consecutive steps read different copies of the
-pools (at least 1 GiB apart) so that no step is served from the 256 MB
-Infinity Cache left warm by the previous one.
+Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload c2|c3|c4|c5]
+
+Default workload (c2): Llama-3-8B-shaped decode.
+- 64 sequences, context lengths U{128..2048}.
+- 32 query / 8 KV heads, head_dim 128.
+- bf16 cache in 16-token blocks, pool = blocks needed + 10 %.
+- One new token per sequence is written, then decoded.
+
+Consecutive steps read different copies of the pools, at least 1 GiB apart
+in total, so no step is served from the 256 MB Infinity Cache that the
+previous step left warm.
+
+The roofline object covers the decode partition kernel.  Its time comes from
+HIP events recorded around that launch alone, on the stream it is launched
+on.  Its HBM traffic comes from rocprofv3 counters taken on the same command.
+`--pmc-summary` turns two counter runs (FETCH_SIZE, then WRITE_SIZE) into the
+committed summary that later bench runs read.
 """
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import os
@@ -28,7 +44,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak, GB/s
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA peak, TFLOP/s
 METRIC = "paged decode attention: seq-tokens/s and achieved HBM GB/s (% of peak)"
+CALIB_BYTES = 1 << 30          # size of the plain copy that calibrates the byte counters
 
 WORKLOAD_TEXT = {
     "c2": "Llama-3-8B-shaped decode: 64 sequences, context U{128..2048}, 32/8 heads, head_dim 128, "
@@ -37,6 +55,9 @@ WORKLOAD_TEXT = {
           "bf16 cache, 16-token blocks, 512-token partitions, keys x3",
     "c4": "shared-prefix decode with copy-on-write: 32 sequences share a 1016-token prefix "
           "(64 blocks), private suffix U{0..512} + 1 token, 32/8 heads, head_dim 128, bf16",
+    "c5": "mixed continuous-batching step at 70B-shaped heads: 240 decodes (lognormal context, "
+          "median 1024, [64, 8192]) + 16 prefill chunks of 256 queries over context U{256..4096}, "
+          "64/8 heads, head_dim 128, bf16, 32-token blocks",
 }
 
 
@@ -48,10 +69,14 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload, algo_bytes):
+def pmc_path(workload):
+    return os.path.join(ROOT, "profiles", f"decode_partition_{workload}_pmc.json")
+
+
+def load_traffic(workload):
     """HBM bytes per partition-kernel launch from the committed counter summary,
     if it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"decode_partition_{workload}_pmc.json")
+    path = pmc_path(workload)
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -61,7 +86,65 @@ def load_traffic(workload, algo_bytes):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, nseq, min_seconds=10.0, max_reps=5):
+# ---- counter summary ---------------------------------------------------------------------
+def _counter_rows(run_dir, counter):
+    """(kernel name, value) of every dispatch in a rocprofv3 --pmc CSV output tree."""
+    rows = []
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") == counter:
+                    rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    if not rows:
+        raise SystemExit(f"no {counter} rows under {run_dir}")
+    return rows
+
+
+def _mean(rows, pred):
+    vals = [v for name, v in rows if pred(name)]
+    if not vals:
+        raise SystemExit("no matching dispatch in the counter output")
+    return sum(vals) / len(vals), len(vals)
+
+
+def pmc_summary(args):
+    """Write the traffic summary for the decode partition kernel.
+
+    The calibration kernel is torch's neg over a 1 GiB float32 tensor, which
+    reads CALIB_BYTES and writes CALIB_BYTES; each counter is scaled by the
+    factor that makes that kernel read exactly its size."""
+    fetch = _counter_rows(args.fetch_dir, "FETCH_SIZE")
+    write = _counter_rows(args.write_dir, "WRITE_SIZE")
+    is_dec = lambda n: "decode_partition_kernel" in n          # noqa: E731
+    is_cal = lambda n: "neg" in n.lower()                       # noqa: E731
+    f_dec, nf = _mean(fetch, is_dec)
+    w_dec, nw = _mean(write, is_dec)
+    f_cal, _ = _mean(fetch, is_cal)
+    w_cal, _ = _mean(write, is_cal)
+    ff = CALIB_BYTES / (f_cal * 1024.0)
+    wf = CALIB_BYTES / (w_cal * 1024.0)
+    d = {
+        "workload": args.workload,
+        "kernel": "decode_partition_kernel",
+        "kernel_source_hash": kernel_source_hash(),
+        "dispatches": [nf, nw],
+        "fetch_kib_per_launch": f_dec,
+        "write_kib_per_launch": w_dec,
+        "calibration": f"torch neg over {CALIB_BYTES} B float32 in the same process: "
+                       f"FETCH_SIZE {f_cal:.0f} KiB, WRITE_SIZE {w_cal:.0f} KiB",
+        "fetch_factor": ff,
+        "write_factor": wf,
+        "hbm_bytes_per_launch": f_dec * 1024.0 * ff + w_dec * 1024.0 * wf,
+        "command": args.command or "",
+    }
+    with open(pmc_path(args.workload), "w") as f:
+        json.dump(d, f, indent=1)
+        f.write("\n")
+    print(json.dumps(d))
+
+
+# ---- CPU oracle baseline -----------------------------------------------------------------
+def cpu_baseline(w, nseq, min_seconds=12.0, max_reps=400):
     """The CPU oracle (fp64, as it stands) decoding the first nseq sequences of
     the workload, repeated until about min_seconds of CPU work."""
     import numpy as np
@@ -89,18 +172,35 @@ def cpu_baseline(w, nseq, min_seconds=10.0, max_reps=5):
                       f"{len(os.sched_getaffinity(0))}"}
 
 
+def prefill_flops(w, clens):
+    """4 * D * Hq flops per (query, visible key) pair of the causal chunks."""
+    tot = 0
+    for C, L in zip(w.chunk_len, clens):
+        # query i sits at position L - C + i and sees L - C + i + 1 keys
+        tot += C * (L - C + 1) + C * (C - 1) // 2
+    return 4 * w.head_dim * w.num_q_heads * tot
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c3", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--partition", type=int, default=512, help="split-K partition (128..512)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=0, help="sequences in the oracle sample (0 = auto)")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="first run one plain 1 GiB device copy (scales the HBM byte counters)")
+                    help="first run a plain 1 GiB elementwise kernel (scales the HBM byte counters)")
+    ap.add_argument("--pmc-summary", action="store_true",
+                    help="summarise two rocprofv3 --pmc runs (no GPU work) into profiles/")
+    ap.add_argument("--fetch-dir")
+    ap.add_argument("--write-dir")
+    ap.add_argument("--command", help="the profiled command, recorded in the summary")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
@@ -123,12 +223,25 @@ def main():
     esz = 2 if w.dtype == "bf16" else 4
 
     # the step's inputs: the tokens the step appends (the new token of every
-    # sequence; for the shared-prefix workload also each private suffix)
+    # sequence; shared-prefix: also each private suffix; mixed: also the chunks)
     rows = np.asarray(st.step_rows)
     k_new = lib_run.torch_stored(w.k_tok[rows], w.dtype).cuda()
     v_new = lib_run.torch_stored(w.v_tok[rows], w.dtype).cuda()
     slots = torch.from_numpy(np.ascontiguousarray(st.step_slots)).cuda()
     pairs = st.step_pairs
+
+    pre = None
+    if w.prefill_seqs:
+        ptab, plens = pa.pa_build_block_tables(st.alloc, w.prefill_seqs, st.max_blocks)
+        pre = {
+            "tables": torch.from_numpy(np.ascontiguousarray(ptab)).cuda(),
+            "lens": torch.from_numpy(np.ascontiguousarray(plens)).cuda(),
+            "qsl": torch.from_numpy(np.concatenate([[0], np.cumsum(w.chunk_len)]).astype(np.int32)).cuda(),
+            "q": lib_run.torch_stored(w.q_pre, w.dtype).cuda(),
+            "max_q": max(w.chunk_len),
+            "flops": prefill_flops(w, [int(x) for x in plens]),
+        }
+        pre["out"] = torch.empty(pre["q"].shape, dtype=torch.float32, device="cuda")
 
     pool_bytes = 2 * pa.pa_cache_pool_bytes(st.desc)
     step_bytes = tokens * 2 * H * D * esz
@@ -144,9 +257,9 @@ def main():
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda") if wsb else None
 
     if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
-        dst.copy_(src)
+        torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
 
@@ -162,19 +275,25 @@ def main():
         if ev is not None:
             ev[1].record()
         pa.pa_decode_reduce(out, st.lens, Hq, D, max_ctx, args.partition, ws)
+        if pre is not None:
+            if ev is not None:
+                ev[2].record()
+            pa.pa_prefill(pre["out"], pre["q"], kc, vc, st.desc, pre["tables"], pre["lens"], pre["qsl"],
+                          pre["max_q"], w.scale)
+            if ev is not None:
+                ev[3].record()
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(args.warmup + i, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    part_ms = [a.elapsed_time(b) for a, b in evs]
+    part_ms = [e[0].elapsed_time(e[1]) for e in evs]
     part_avg_s = float(np.mean(part_ms)) / 1e3
     assert torch.isfinite(out).all()
 
@@ -184,7 +303,6 @@ def main():
     nblocks = int(np.sum(-(-lens // w.block_size)))
     algo = tokens * 2 * H * D * esz + B * Hq * D * (esz + 4) + 4 * nblocks + 4 * B
     achieved = algo / part_avg_s / 1e9
-    traffic = load_traffic(args.workload, algo)
     res = {
         "metric": METRIC,
         "value": tokens / (ms_per_step / 1e3),
@@ -201,14 +319,26 @@ def main():
         "config": {"workload": WORKLOAD_TEXT[args.workload], "sequences": B,
                    "context_tokens": tokens, "q_heads": Hq, "kv_heads": H, "head_dim": D,
                    "block_size": w.block_size, "partition": args.partition, "pool_copies": copies,
-                   "step": ("copy_blocks + " if pairs else "") + "cache_write + decode_partitions + decode_reduce"},
+                   "step": ("copy_blocks + " if pairs else "") +
+                           "cache_write + decode_partitions + decode_reduce" +
+                           (" + prefill" if pre is not None else "")},
         "roofline": {"bound": "hbm", "kernel": "decode_partition_kernel", "achieved": achieved,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
-                     "traffic": traffic, "algorithmic_bytes_per_launch": algo,
-                     "avg_launch_us": part_avg_s * 1e6,
+                     "traffic": load_traffic(args.workload), "algorithmic_bytes_per_launch": algo,
+                     "avg_launch_us": part_avg_s * 1e6, "p10_us": float(np.percentile(part_ms, 10)) * 1e3,
+                     "p90_us": float(np.percentile(part_ms, 90)) * 1e3,
                      "kernel_source_hash": kernel_source_hash()},
         "decode_gbs_whole_step": algo / (ms_per_step / 1e3) / 1e9,
     }
+    if pre is not None:
+        pre_ms = [e[2].elapsed_time(e[3]) for e in evs]
+        pre_s = float(np.mean(pre_ms)) / 1e3
+        tf = pre["flops"] / pre_s / 1e12
+        assert torch.isfinite(pre["out"]).all()
+        res["prefill"] = {"bound": "mfma", "kernel": "prefill_kernel", "achieved": tf,
+                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
+                          "flops_per_launch": pre["flops"], "avg_launch_us": pre_s * 1e6,
+                          "query_tokens": int(sum(w.chunk_len))}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         nseq = args.cpu_seqs or len(w.decode_seqs)

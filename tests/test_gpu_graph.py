@@ -1,0 +1,92 @@
+"""The device calls captured in a HIP graph: every replay must equal the eager
+result bit for bit.
+
+The library launches only kernels (no memset or copy nodes), so a captured
+step is a chain of kernel nodes.  The graph is replayed several times with
+eager work and synchronizations in between, and each replay is checked.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_424_amd as pa
+import workloads
+from tests import lib_run
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+@pytest.mark.parametrize("name,part", [("c2", 512), ("c3", 256), ("c1", 128)])
+def test_decode_graph_replays_match_eager(name, part):
+    _announce(f"graph decode {name} part {part}")
+    w = workloads.make(name, small=True)
+    st = lib_run.build(w)
+    B, Hq, D = st.q.shape
+    eager = lib_run.decode(w, st, partition_size=part)
+    out = torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    wsb = pa.pa_decode_workspace_bytes(B, Hq, D, st.max_ctx, part)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pa.pa_decode(out, st.q, st.kc, st.vc, st.desc, st.tables, st.lens, st.max_ctx, w.scale,
+                     partition_size=part, workspace=ws)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), rep
+        # eager work between replays, on the same buffers the graph reads
+        again = lib_run.decode(w, st, partition_size=part)
+        torch.cuda.synchronize()
+        assert torch.equal(again, eager)
+
+
+def test_step_graph_with_cache_write_and_prefill():
+    _announce("graph mixed step c5 small")
+    w = workloads.make("c5", small=True)
+    st = lib_run.build(w)
+    # eager reference: the pools after build() already hold the step's tokens
+    eager_dec = lib_run.decode(w, st)
+    eager_pre = lib_run.prefill(w, st)
+    kbits = lib_run.pool_bits(st.kc, w.dtype).copy()
+    vbits = lib_run.pool_bits(st.vc, w.dtype).copy()
+
+    rows = np.asarray(st.step_rows)
+    k_new = lib_run.torch_stored(w.k_tok[rows], w.dtype).cuda()
+    v_new = lib_run.torch_stored(w.v_tok[rows], w.dtype).cuda()
+    slots = torch.from_numpy(np.ascontiguousarray(st.step_slots)).cuda()
+    ptab, plens = pa.pa_build_block_tables(st.alloc, w.prefill_seqs, st.max_blocks)
+    ptab = torch.from_numpy(np.ascontiguousarray(ptab)).cuda()
+    plens = torch.from_numpy(np.ascontiguousarray(plens)).cuda()
+    qsl = torch.from_numpy(np.concatenate([[0], np.cumsum(w.chunk_len)]).astype(np.int32)).cuda()
+    qp = lib_run.torch_stored(w.q_pre, w.dtype).cuda()
+    B, Hq, D = st.q.shape
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    pout = torch.empty(qp.shape, dtype=torch.float32, device="cuda")
+    wsb = pa.pa_decode_workspace_bytes(B, Hq, D, st.max_ctx, 0)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pa.pa_cache_write(st.kc, st.vc, st.desc, k_new, v_new, slots)
+        pa.pa_decode(out, st.q, st.kc, st.vc, st.desc, st.tables, st.lens, st.max_ctx, w.scale,
+                     workspace=ws)
+        pa.pa_prefill(pout, qp, st.kc, st.vc, st.desc, ptab, plens, qsl, max(w.chunk_len), w.scale)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        pout.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager_dec), rep
+        assert torch.equal(pout, eager_pre), rep
+        # rewriting the same tokens leaves the pools unchanged, bit for bit
+        assert np.array_equal(lib_run.pool_bits(st.kc, w.dtype), kbits)
+        assert np.array_equal(lib_run.pool_bits(st.vc, w.dtype), vbits)
+        lib_run.decode(w, st)
+        torch.cuda.synchronize()
