@@ -187,7 +187,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c2", choices=sorted(WORKLOAD_TEXT))
-    ap.add_argument("--partition", type=int, default=512, help="split-K partition (128..512)")
+    ap.add_argument("--partition", type=int, default=None,
+                    help="split-K partition in tokens (a multiple of 32), or 0 for the balanced split; "
+                         "default: 512 for the long-context workload (its stated partition), else 0")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=0, help="sequences in the oracle sample (0 = auto)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -213,6 +215,8 @@ def main():
     import workloads
     from tests import lib_run
 
+    if args.partition is None:
+        args.partition = 512 if args.workload == "c3" else 0
     torch.cuda.set_device(0)
     print(f"[bench] workload {args.workload}: generating inputs", file=sys.stderr, flush=True)
     w = workloads.make(args.workload)

@@ -1,4 +1,5 @@
-// Paged decode attention for gfx950: split-K partitions + a rescaling reduce.
+// Paged decode attention for gfx950: a persistent split-K kernel plus a
+// rescaling reduce.
 //
 // What is computed: for every sequence s and query head h, attention of the
 // one new query over the sequence's whole context, read block by block through
@@ -8,14 +9,34 @@
 // Paging changes where K/V live, not the result, so the kernels must reach
 // softmax(scale * K q) V of the gathered context.
 //
-// Work decomposition.  One workgroup (4 waves) per (sequence, kv head,
-// partition of PART = 128 * NCH tokens).  Wave w takes the 32-token chunks
-// w, w+4, w+8, ... of the partition, so a short last partition still spreads
-// over the waves.  Each wave keeps an online softmax (running max m, sum l and
-// unnormalised output) per query head of the kv head's group; the four waves
-// are merged through LDS at the end.  A sequence with one partition gets its
-// output here; longer ones leave (m, l, output) per partition in the
-// workspace for the reduce kernel.
+// Work split.  The context of one (sequence, kv head) is cut into pieces; each
+// piece yields a partial (running max m, sum l, unnormalised output o) per
+// query head of the group, and the reduce kernel merges the pieces.  A head
+// whose context is a single piece gets its final output directly.  Two ways
+// to cut:
+//   * balanced (partition_size == 0, the default): the (sequence, kv head,
+//     32-token chunk) space is laid end to end and cut into equal ranges, one
+//     per workgroup, so every workgroup streams the same number of bytes
+//     whatever the length mix.  A range may cover the tail of one (sequence,
+//     head), several short ones and the head of the next.  Where the cuts fall
+//     depends on every length in the batch (and on the number of compute
+//     units), so a row's rounding may change with the rest of the batch.
+//     The grid is persistent: as many workgroups as the chip holds at once.
+//     Each first reads every context length into LDS and scans them, so no
+//     workgroup is spent on an empty partition and no host-side length is
+//     needed.
+//   * fixed partitions (partition_size = P > 0): pieces start at absolute
+//     positions 0, P, 2P, ...; a row's result depends on its own length only.
+//     One workgroup per (sequence, kv head, partition), dispatched by the
+//     hardware as slots free up, which suits batches of similar lengths.
+// Scheduling is static on purpose: handing out work through an atomic
+// counter measured 30-45 % slower on this chip, where device-scope atomics on
+// one word from all eight XCDs take microseconds each.
+
+// Inside a partition.  The four waves take its 32-token chunks round robin, in
+// windows of 16 chunks (512 tokens) whose block ids are staged in LDS (double
+// buffered, one barrier per window).  Each wave keeps an online softmax per
+// query head and the four waves are merged through LDS at the end.
 //
 // Matrix cores.  The query group (G <= 16 heads) against a 16-token K tile is
 // a dense contraction, done as S^T[token][head] = K[token][:] . Q^T with
@@ -31,9 +52,12 @@
 // the product keeps ~16 bits of the fp32 weight (one extra MFMA per step; the
 // kernel is bound by HBM, not by the matrix cores).
 //
-// Every (s, h) result depends only on logical positions, never on physical
-// block ids, and uses no atomics: outputs are bit-identical under any
+// A result depends on logical positions and lengths only, never on physical
+// block ids, and no atomics are used: outputs are bit-identical under any
 // relabelling of blocks and whether a prefix is shared or duplicated.
+
+#include <algorithm>
+#include <atomic>
 
 #include "pa_internal.h"
 
@@ -47,7 +71,13 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kChunk = 32;       // tokens per wave step
+constexpr int kChunk = 32;                              // tokens per wave step
+constexpr int kWinChunks = 16;                          // chunks per window (512 tokens)
+constexpr int kMinBlock = 8;                            // smallest supported block size
+constexpr int kWinBlocks = kWinChunks * kChunk / kMinBlock + 1;   // block ids a window can touch
+constexpr int kMaxSeqsPerLaunch = 1024;                 // lengths scanned in LDS per launch
+constexpr int kMinPieceChunks = 4;                      // balanced: at least 128 tokens per range
+constexpr int kSeqsPerThread = kMaxSeqsPerLaunch / kThreads;
 
 struct DecodeArgs {
     void* out;
@@ -56,10 +86,13 @@ struct DecodeArgs {
     const void* vc;
     const int32_t* tables;
     const int32_t* lens;
-    float* ws_acc;     // [B][Hq][P][D]
-    float2* ws_ml;     // [B][Hq][P] (max in log2 units, sum)
-    int32_t B, Hq, H, G, bs, N, maxb, max_ctx, P;
-    float scale_log2;  // scale * log2(e): logits are kept in base-2 units
+    float* ws_acc;     // [B][Hq][pmax][D]
+    float2* ws_ml;     // [B][Hq][pmax] (max in log2 units, sum)
+    int32_t* ws_np;    // [B][Hq] pieces of the (sequence, head)
+    int32_t B, Hq, H, G, bs, N, maxb, max_ctx;
+    int32_t part_chunks;   // > 0: fixed partitions of this many 32-token chunks; 0: balanced
+    int32_t pmax;          // piece slots per (sequence, head) in the workspace
+    float scale_log2;      // scale * log2(e): logits are kept in base-2 units
     int32_t out_bf16;
 };
 
@@ -95,6 +128,41 @@ __device__ __forceinline__ u32x4 ldg_nt(const char* p) {
 
 constexpr u32x4 kZero4 = {0u, 0u, 0u, 0u};
 
+// Exclusive prefix sum of one value per thread over the workgroup; *total
+// receives the sum.  Every thread must call it.
+__device__ __forceinline__ int block_exscan(int v, int* s_tmp, int* total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) s_tmp[w] = x;
+    __syncthreads();
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+        const int t = s_tmp[i];
+        before += i < w ? t : 0;
+        tot += t;
+    }
+    __syncthreads();
+    *total = tot;
+    return before + x - v;
+}
+
+// Last index s in [0, n) with cum[s] <= x, for a non-decreasing cum[0..n] with
+// cum[0] <= x < cum[n]: the sequence whose items contain item x.
+__device__ __forceinline__ int find_seq(const int* cum, int n, int x) {
+    int lo = 0, hi = n;                 // cum[lo] <= x < cum[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (cum[mid] <= x) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
 // Per-lane registers of one 32-token chunk.
 template <bool BF16, int D>
 struct ChunkRegs {
@@ -106,19 +174,15 @@ struct ChunkRegs {
     u32x4 v[VV];
 };
 
-template <bool BF16, int D, int NCH>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void decode_partition_kernel(
+// fp32 caches at head_dim 128 hold twice the registers per chunk and run at
+// two waves per SIMD; every other variant at three.
+template <bool BF16, int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 || D == 64 ? 3 : 2))) void decode_partition_kernel(
     DecodeArgs a) {
-    constexpr int PART = kChunk * kWaves * NCH;
     constexpr int ES = BF16 ? 2 : 4;
     using Regs = ChunkRegs<BF16, D>;
     constexpr int MT = D / 16;                    // output channel tiles
-
-    const int u = xcd_remap(blockIdx.x, gridDim.x);
-    const int s = u % a.B;
-    const int pg = u / a.B;
-    const int p = pg % a.P;
-    const int g = pg / a.P;
+    constexpr int QV = BF16 ? D / 32 : D / 16;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -126,261 +190,351 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     const int j = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int G = a.G;
-
-    const int L = a.lens[s];
-    const bool bad_len = L < 1 || L > a.max_ctx || static_cast<int64_t>(L) > static_cast<int64_t>(a.maxb) * a.bs;
-    const int nparts = bad_len ? 1 : (L + PART - 1) / PART;
-    if (p >= nparts) return;
-
+    const int H = a.H;
+    const int B = a.B;
+    const int bs = a.bs;
     const float kNaN = __builtin_nanf("");
-    if (bad_len) {
-        // Invalid length: NaN for the group's heads, nothing read.
+
+    // ---- LDS: (balanced split) lengths and their prefix sums; wave-merge buffers ----
+    const bool fixed = a.part_chunks > 0;
+    extern __shared__ int s_dyn[];
+    int* s_len = s_dyn;                           // [B]  L, or -1 for an invalid length
+    int* s_cum = s_len + B;                       // [B+1] chunks per head before sequence s
+    float* s_acc = reinterpret_cast<float*>(fixed ? s_dyn : s_cum + B + 1);   // [4][G][D+4]
+    __shared__ int s_blk[2][kWinBlocks];
+    __shared__ float s_m[kWaves][16];
+    __shared__ float s_l[kWaves][16];
+    __shared__ int s_tmp[kWaves];
+
+    const int64_t tile_elems = static_cast<int64_t>(H) * bs * D;   // one block, all heads
+    int buf = 0;                                                    // s_blk buffer in use
+
+    // One partition: chunks [cb, ce) of (sequence s, kv head g), the piece-th
+    // of its npieces partitions.
+    auto process = [&](int s, int g, int L, int cb, int ce, int piece, int npieces) {
+        const char* kbase = static_cast<const char*>(a.kc) + static_cast<int64_t>(g) * bs * D * ES;
+        const char* vbase = static_cast<const char*>(a.vc) + static_cast<int64_t>(g) * D * bs * ES;
+        const int nblk_seq = (L + bs - 1) / bs;
+        const int32_t* trow = a.tables + static_cast<int64_t>(s) * a.maxb;
+
+        // Query operand: lane (j, r) holds head r's channels for k-group j.
+        u32x4 qreg[QV];
+        {
+            const char* qrow = static_cast<const char*>(a.q) +
+                               ((static_cast<int64_t>(s) * a.Hq + g * G + r) * D) * ES;
+#pragma unroll
+            for (int c = 0; c < QV; ++c) {
+                // bf16: channels c*32 + j*8 .. +8;  fp32: channels j*(D/4) + 4c .. +4
+                const int d0 = BF16 ? c * 32 + j * 8 : j * (D / 4) + 4 * c;
+                qreg[c] = r < G ? *reinterpret_cast<const u32x4*>(qrow + static_cast<int64_t>(d0) * ES)
+                                : kZero4;
+            }
+        }
+
+        float m_run = -INFINITY;
+        float l_run = 0.f;
+        f32x4_t acc[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+        // Loads are unconditional: every address is inside the pool (ids of
+        // blocks past the sequence's end were replaced by block 0), so no load
+        // sits behind a divergent branch and all of a chunk's loads issue back
+        // to back.  Rows past the context end are dealt with when the chunk is
+        // consumed: their logits are selected to -inf and their values to 0.
+        auto load_chunk = [&](int ci, int fb, const int* blk_ids, Regs& R) {
+            const int tc = ci * kChunk;               // absolute position of the chunk
+            // K: row r of tile t is chunk token 8*(r>>2) + (r&3) + 4t.
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int tp = tc + 8 * (r >> 2) + (r & 3) + 4 * t;
+                const int64_t blk = blk_ids[tp / bs - fb];
+                const char* row = kbase + ((blk * tile_elems) + static_cast<int64_t>(tp % bs) * D) * ES;
+#pragma unroll
+                for (int c = 0; c < Regs::KV; ++c) {
+                    const int d0 = BF16 ? c * 32 + j * 8 : j * (D / 4) + 4 * c;
+                    R.k[t][c] = ldg_nt(row + static_cast<int64_t>(d0) * ES);
+                }
+            }
+            // V: lane (j, r) reads tokens 8j..8j+7 of channel mt*16 + r.
+            const int tp0 = tc + 8 * j;
+            const int64_t blk = blk_ids[tp0 / bs - fb];
+            const char* vb = vbase + (blk * tile_elems + tp0 % bs) * ES;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const int64_t ch = mt * 16 + r;
+                if (BF16) {
+                    R.v[mt] = ldg_nt(vb + ch * bs * ES);
+                } else {
+                    R.v[2 * mt] = ldg_nt(vb + ch * bs * ES);
+                    R.v[2 * mt + 1] = ldg_nt(vb + ch * bs * ES + 16);
+                }
+            }
+        };
+
+        auto compute_chunk = [&](int ci, const Regs& R) {
+            const int tc = ci * kChunk;
+            // ---- logits: S^T[token][head] for the chunk's two 16-row tiles ----
+            f32x4_t st[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                f32x4_t c4 = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (BF16) {
+#pragma unroll
+                    for (int c = 0; c < Regs::KV; ++c)
+                        c4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.k[t][c]), as_bf16x8(qreg[c]),
+                                                                     c4, 0, 0, 0);
+                } else {
+#pragma unroll
+                    for (int c = 0; c < Regs::KV; ++c) {
+                        const u32x4 kk = R.k[t][c], qq = qreg[c];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            c4 = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kk[e]),
+                                                                      __uint_as_float(qq[e]), c4, 0, 0, 0);
+                    }
+                }
+                st[t] = c4;
+            }
+            // lane (j, r): head r, chunk tokens 8j + e with e = 4t + i
+            float sv[8];
+            const int ntok = L - (tc + 8 * j);                // valid tokens among this lane's 8
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = st[e >> 2][e & 3] * a.scale_log2;
+                sv[e] = e < ntok ? x : -INFINITY;
+            }
+            float cm = sv[0];
+#pragma unroll
+            for (int e = 1; e < 8; ++e) cm = fmaxf(cm, sv[e]);
+            cm = fmaxf(cm, __shfl_xor(cm, 16));
+            cm = fmaxf(cm, __shfl_xor(cm, 32));
+            // every chunk of a partition holds at least one valid token, so cm is finite
+            const float m_new = fmaxf(m_run, cm);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            float pv[8];
+            float psum = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                pv[e] = __builtin_amdgcn_exp2f(sv[e] - m_new);
+                psum += pv[e];
+            }
+            l_run = l_run * alpha + psum;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
+            // ---- values: O^T[channel][head] += V^T[channel][token] . P^T ----
+            // A weight of 0 does not cancel a NaN value (never-written slots past
+            // the context end), so those values are zeroed by select.
+            Regs Rm = R;
+            if (tc + kChunk > L) {
+#pragma unroll
+                for (int x = 0; x < Regs::VV; ++x) {
+                    if constexpr (BF16)
+                        Rm.v[x] = keep_first_bf16(R.v[x], ntok);
+                    else
+                        Rm.v[x] = keep_first_f32(R.v[x], (x & 1) ? ntok - 4 : ntok);
+                }
+            }
+            if constexpr (BF16) {
+                bf16x8_t ph, pl;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const __bf16 hi = static_cast<__bf16>(pv[e]);
+                    ph[e] = hi;
+                    pl[e] = static_cast<__bf16>(pv[e] - static_cast<float>(hi));
+                }
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Rm.v[mt]), ph, acc[mt], 0, 0, 0);
+                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Rm.v[mt]), pl, acc[mt], 0, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const u32x4 v0 = Rm.v[2 * mt], v1 = Rm.v[2 * mt + 1];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(e < 4 ? v0[e] : v1[e - 4]),
+                                                                       pv[e], acc[mt], 0, 0, 0);
+                }
+            }
+        };
+
+        // Windows of up to 16 chunks.  The window's block ids go to one of two
+        // LDS buffers, so one barrier per window suffices: a buffer is written
+        // again only two windows later, after every wave has passed the barrier
+        // that follows its last use.  Block ids past the sequence's end are
+        // replaced by block 0; an id outside the pool makes the partition NaN and
+        // is never dereferenced.
+
+        int bad = 0;
+        for (int wb = cb; wb < ce; wb += kWinChunks) {
+            const int we = min(ce, wb + kWinChunks);
+            const int fb = (wb * kChunk) / bs;
+            const int nb = (we * kChunk - 1) / bs - fb + 1;
+            int* ids = s_blk[buf];
+            if (tid < nb) {
+                const int b = fb + tid;
+                int id = 0;
+                if (b < nblk_seq) {
+                    id = trow[b];
+                    if (id < 0 || id >= a.N) {
+                        bad = 1;
+                        id = 0;
+                    }
+                }
+                ids[tid] = id;
+            }
+            bad = __syncthreads_or(bad);
+            // Latency is hidden by occupancy (three workgroups per CU), not by
+            // a register double buffer: holding a second chunk needs ~280
+            // registers, which spills even at two waves per SIMD.
+            for (int ci = wb + w; ci < we; ci += kWaves) {
+                Regs R;
+                load_chunk(ci, fb, ids, R);
+                compute_chunk(ci, R);
+            }
+            buf ^= 1;
+        }
+
+        // ---- merge the four waves through LDS ----
+        const int rowstride = D + 4;
+        float l_tot = l_run + __shfl_xor(l_run, 16);
+        l_tot += __shfl_xor(l_tot, 32);
+        if (j == 0) {
+            s_m[w][r] = m_run;
+            s_l[w][r] = l_tot;
+        }
+        if (r < G) {
+            float* dst = s_acc + (w * G + r) * rowstride;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst[mt * 16 + 4 * j + i] = acc[mt][i];
+        }
+        __syncthreads();
+
         for (int e = tid; e < G * D; e += kThreads) {
             const int h = e / D, d = e % D;
-            store_out(a.out, (static_cast<int64_t>(s) * a.Hq + g * G + h) * D + d, kNaN, a.out_bf16);
+            // a wave with no chunk in this partition has m = -inf and contributes 0
+            float M = s_m[0][h];
+#pragma unroll
+            for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, s_m[ww][h]);
+            float o = 0.f, l = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < kWaves; ++ww) {
+                const float f = __builtin_amdgcn_exp2f(s_m[ww][h] - M);
+                o += f * s_acc[(ww * G + h) * rowstride + d];
+                l += f * s_l[ww][h];
+            }
+            const int64_t sh = static_cast<int64_t>(s) * a.Hq + g * G + h;
+            if (npieces == 1) {
+                store_out(a.out, sh * D + d, bad ? kNaN : o / l, a.out_bf16);
+            } else {
+                a.ws_acc[(sh * a.pmax + piece) * D + d] = bad ? kNaN : o;
+                if (d == 0) a.ws_ml[sh * a.pmax + piece] = bad ? make_float2(kNaN, kNaN) : make_float2(M, l);
+            }
+            if (piece == 0 && d == 0 && a.ws_np) a.ws_np[sh] = npieces;
         }
+    };
+
+    if (fixed) {
+        // One workgroup per (sequence, kv head, partition), dispatched by the
+        // hardware as slots free up; partitions past a sequence's end exit at
+        // once.  An invalid length gives NaN for the head group, written by
+        // the workgroup of partition 0.
+        const int u = xcd_remap(blockIdx.x, gridDim.x);
+        const int s = u % B;
+        const int p = (u / B) % a.pmax;
+        const int g = u / (B * a.pmax);
+        const int part_tokens = a.part_chunks * kChunk;
+        const int L = a.lens[s];
+        if (L < 1 || L > a.max_ctx) {
+            if (p == 0) {
+                for (int e = tid; e < G * D; e += kThreads)
+                    store_out(a.out, (static_cast<int64_t>(s) * a.Hq + g * G) * D + e, kNaN, a.out_bf16);
+                if (a.ws_np && tid < G) a.ws_np[static_cast<int64_t>(s) * a.Hq + g * G + tid] = 0;
+            }
+            return;
+        }
+        const int np = (L + part_tokens - 1) / part_tokens;
+        if (p >= np) return;
+        const int cb = p * a.part_chunks;
+        process(s, g, L, cb, min((L + kChunk - 1) / kChunk, cb + a.part_chunks), p, np);
         return;
     }
 
-    // Block ids of this partition, validated once: a bad id makes the whole
-    // group's output NaN and is never dereferenced.
-    __shared__ int s_blk[PART / 4];
-    const int bs = a.bs;
-    const int nbp = PART / bs;                    // blocks per partition (bs divides PART)
-    const int nblk_seq = (L + bs - 1) / bs;
-    int bad = 0;
-    for (int i = tid; i < nbp; i += kThreads) {
-        const int b = p * nbp + i;
-        int id = 0;
-        if (b < nblk_seq) {
-            id = a.tables[static_cast<int64_t>(s) * a.maxb + b];
-            if (id < 0 || id >= a.N) {
-                bad = 1;
-                id = 0;
-            }
-        }
-        s_blk[i] = id;
-    }
-    bad = __syncthreads_or(bad);
-
-    const int64_t tile_elems = static_cast<int64_t>(a.H) * bs * D;   // one block, all heads
-    const char* kbase = static_cast<const char*>(a.kc) + static_cast<int64_t>(g) * bs * D * ES;
-    const char* vbase = static_cast<const char*>(a.vc) + static_cast<int64_t>(g) * D * bs * ES;
-
-    // Query operand: lane (j, r) holds head r's channels for k-group j.
-    constexpr int QV = BF16 ? D / 32 : D / 16;
-    u32x4 qreg[QV];
+    // ---- balanced split: scan the lengths ----
     {
-        const char* qrow = static_cast<const char*>(a.q) +
-                           ((static_cast<int64_t>(s) * a.Hq + g * G + r) * D) * ES;
+        int cnt[kSeqsPerThread];
+        int sum = 0;
 #pragma unroll
-        for (int c = 0; c < QV; ++c) {
-            // bf16: channels c*32 + j*8 .. +8;  fp32: channels j*(D/4) + 4c .. +4
-            const int d0 = BF16 ? c * 32 + j * 8 : j * (D / 4) + 4 * c;
-            qreg[c] = r < G ? *reinterpret_cast<const u32x4*>(qrow + static_cast<int64_t>(d0) * ES)
-                            : kZero4;
+        for (int i = 0; i < kSeqsPerThread; ++i) {
+            const int s = tid * kSeqsPerThread + i;
+            int L = s < B ? a.lens[s] : -1;
+            // the host guarantees max_ctx <= maxb * bs, so a valid L needs no
+            // other bound to stay inside the block table
+            const bool ok = L >= 1 && L <= a.max_ctx;
+            if (!ok) L = -1;
+            if (s < B) s_len[s] = L;
+            cnt[i] = ok ? (L + kChunk - 1) / kChunk : 0;      // chunks per head
+            sum += cnt[i];
         }
+        int tot;
+        int pre = block_exscan(sum, s_tmp, &tot);
+#pragma unroll
+        for (int i = 0; i < kSeqsPerThread; ++i) {
+            const int s = tid * kSeqsPerThread + i;
+            if (s < B) s_cum[s] = pre;
+            pre += cnt[i];
+        }
+        if (tid == 0) s_cum[B] = tot;
+        __syncthreads();
     }
 
-    const int part0 = p * PART;                   // first absolute position of the partition
-
-    // Loads are unconditional: every address is inside the pool (ids of blocks
-    // past the sequence's end were replaced by block 0 above), so no load sits
-    // behind a divergent branch and all of a chunk's loads issue back to back.
-    // Rows past the context end are dealt with when the chunk is consumed: their
-    // logits are selected to -inf and their values to 0.
-    auto load_chunk = [&](int ci, Regs& R) {
-        const int tc = ci * kChunk;               // chunk offset inside the partition
-        // K: row r of tile t is chunk token 8*(r>>2) + (r&3) + 4t.
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int tp = tc + 8 * (r >> 2) + (r & 3) + 4 * t;
-            const int64_t blk = s_blk[tp / bs];
-            const char* row = kbase + ((blk * tile_elems) + static_cast<int64_t>(tp % bs) * D) * ES;
-#pragma unroll
-            for (int c = 0; c < Regs::KV; ++c) {
-                const int d0 = BF16 ? c * 32 + j * 8 : j * (D / 4) + 4 * c;
-                R.k[t][c] = ldg_nt(row + static_cast<int64_t>(d0) * ES);
-            }
-        }
-        // V: lane (j, r) reads tokens 8j..8j+7 of channel mt*16 + r.
-        const int tp0 = tc + 8 * j;
-        const int64_t blk = s_blk[tp0 / bs];
-        const char* vb = vbase + (blk * tile_elems + tp0 % bs) * ES;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int64_t ch = mt * 16 + r;
-            if (BF16) {
-                R.v[mt] = ldg_nt(vb + ch * bs * ES);
-            } else {
-                R.v[2 * mt] = ldg_nt(vb + ch * bs * ES);
-                R.v[2 * mt + 1] = ldg_nt(vb + ch * bs * ES + 16);
-            }
-        }
-    };
-
-    float m_run = -INFINITY;
-    float l_run = 0.f;
-    f32x4_t acc[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    auto compute_chunk = [&](int ci, const Regs& R) {
-        const int tc = ci * kChunk;
-        // ---- logits: S^T[token][head] for the chunk's two 16-row tiles ----
-        f32x4_t st[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            f32x4_t c4 = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (BF16) {
-#pragma unroll
-                for (int c = 0; c < Regs::KV; ++c)
-                    c4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.k[t][c]), as_bf16x8(qreg[c]),
-                                                                 c4, 0, 0, 0);
-            } else {
-#pragma unroll
-                for (int c = 0; c < Regs::KV; ++c) {
-                    const u32x4 kk = R.k[t][c], qq = qreg[c];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        c4 = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kk[e]), __uint_as_float(qq[e]),
-                                                                  c4, 0, 0, 0);
-                }
-            }
-            st[t] = c4;
-        }
-        // lane (j, r): head r, chunk tokens 8j + e with e = 4t + i
-        float sv[8];
-        const int ntok = L - (part0 + tc + 8 * j);         // valid tokens among this lane's 8
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float x = st[e >> 2][e & 3] * a.scale_log2;
-            sv[e] = e < ntok ? x : -INFINITY;
-        }
-        float cm = sv[0];
-#pragma unroll
-        for (int e = 1; e < 8; ++e) cm = fmaxf(cm, sv[e]);
-        cm = fmaxf(cm, __shfl_xor(cm, 16));
-        cm = fmaxf(cm, __shfl_xor(cm, 32));
-        // the chunk holds at least one valid token, so cm is finite
-        const float m_new = fmaxf(m_run, cm);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        float pv[8];
-        float psum = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            pv[e] = __builtin_amdgcn_exp2f(sv[e] - m_new);
-            psum += pv[e];
-        }
-        l_run = l_run * alpha + psum;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
-        // ---- values: O^T[channel][head] += V^T[channel][token] . P^T ----
-        // A weight of 0 does not cancel a NaN value (never-written slots past
-        // the context end), so those values are zeroed by select.
-        Regs Rm = R;
-        if (part0 + tc + kChunk > L) {
-#pragma unroll
-            for (int x = 0; x < Regs::VV; ++x) {
-                if constexpr (BF16)
-                    Rm.v[x] = keep_first_bf16(R.v[x], ntok);
-                else
-                    Rm.v[x] = keep_first_f32(R.v[x], (x & 1) ? ntok - 4 : ntok);
-            }
-        }
-        if constexpr (BF16) {
-            bf16x8_t ph, pl;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const __bf16 h = static_cast<__bf16>(pv[e]);
-                ph[e] = h;
-                pl[e] = static_cast<__bf16>(pv[e] - static_cast<float>(h));
-            }
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Rm.v[mt]), ph, acc[mt], 0, 0, 0);
-                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Rm.v[mt]), pl, acc[mt], 0, 0, 0);
-            }
-        } else {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const u32x4 v0 = Rm.v[2 * mt], v1 = Rm.v[2 * mt + 1];
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(e < 4 ? v0[e] : v1[e - 4]), pv[e],
-                                                                   acc[mt], 0, 0, 0);
-            }
-        }
-    };
-
-    // Chunk loop.  Latency is hidden by occupancy, not by an explicit register
-    // double buffer: the kernel is held to >= 3 waves per SIMD (at most ~168
-    // registers each), which leaves the scheduler room to start a chunk's
-    // sixteen 16-byte loads early while keeping three workgroups resident per
-    // CU -- one workgroup's start-up (length, block ids, query) and merge then
-    // overlap the others' streaming.  An explicit two-chunk buffer needs ~260
-    // registers and one wave per SIMD, and measured 25 % slower.
-    const int first_empty = (L - part0 + kChunk - 1) / kChunk;   // chunks >= this are empty
-#pragma unroll
-    for (int k = 0; k < NCH; ++k) {
-        const int ci = w + kWaves * k;
-        if (ci >= first_empty) break;
-        Regs R;
-        load_chunk(ci, R);
-        compute_chunk(ci, R);
+    // invalid lengths: NaN for every head and no piece (workgroup s % grid)
+    for (int s = blockIdx.x; s < B; s += gridDim.x) {
+        if (s_len[s] >= 0) continue;
+        for (int e = tid; e < a.Hq * D; e += kThreads)
+            store_out(a.out, static_cast<int64_t>(s) * a.Hq * D + e, kNaN, a.out_bf16);
+        if (a.ws_np)
+            for (int h = tid; h < a.Hq; h += kThreads) a.ws_np[static_cast<int64_t>(s) * a.Hq + h] = 0;
     }
 
-    // ---- merge the four waves through LDS ----
-    extern __shared__ float s_dyn[];
-    const int rowstride = D + 4;
-    float* s_acc = s_dyn;                                   // [4][G][D+4]
-    __shared__ float s_m[kWaves][16];
-    __shared__ float s_l[kWaves][16];
-    float l_tot = l_run + __shfl_xor(l_run, 16);
-    l_tot += __shfl_xor(l_tot, 32);
-    if (j == 0) {
-        s_m[w][r] = m_run;
-        s_l[w][r] = l_tot;
-    }
-    if (r < G) {
-        float* dst = s_acc + (w * G + r) * rowstride;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dst[mt * 16 + 4 * j + i] = acc[mt][i];
-    }
-    __syncthreads();
-
-    const bool single = nparts == 1;
-    for (int e = tid; e < G * D; e += kThreads) {
-        const int h = e / D, d = e % D;
-        float M = s_m[0][h];
-#pragma unroll
-        for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, s_m[ww][h]);
-        float o = 0.f, l = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) {
-            const float f = __builtin_amdgcn_exp2f(s_m[ww][h] - M);
-            o += f * s_acc[(ww * G + h) * rowstride + d];
-            l += f * s_l[ww][h];
-        }
-        const int64_t sh = static_cast<int64_t>(s) * a.Hq + g * G + h;
-        if (single) {
-            store_out(a.out, sh * D + d, bad ? kNaN : o / l, a.out_bf16);
-        } else {
-            a.ws_acc[(sh * a.P + p) * D + d] = bad ? kNaN : o;
-            if (d == 0) a.ws_ml[sh * a.P + p] = bad ? make_float2(kNaN, kNaN) : make_float2(M, l);
-        }
+    // Ranges of Cw chunks over the (sequence, kv head, chunk) space, laid out
+    // sequence by sequence and head by head.  The workgroup index is remapped
+    // so that neighbouring ranges run on the same XCD.
+    const int64_t T = static_cast<int64_t>(H) * s_cum[B];
+    const int64_t grid = gridDim.x;
+    const int64_t Cw = max(static_cast<int64_t>(kMinPieceChunks), (T + grid - 1) / grid);
+    const int64_t wr = xcd_remap(blockIdx.x, gridDim.x);
+    int64_t pos = wr * Cw;
+    const int64_t end = min(T, pos + Cw);
+    if (pos >= end) return;
+    int s = find_seq(s_cum, B, static_cast<int>(pos / H));
+    while (pos < end) {
+        const int n = s_cum[s + 1] - s_cum[s];          // chunks per head of sequence s
+        const int64_t base = static_cast<int64_t>(H) * s_cum[s];
+        const int g = static_cast<int>((pos - base) / n);
+        const int off = static_cast<int>((pos - base) % n);
+        const int take = static_cast<int>(min(static_cast<int64_t>(n - off), end - pos));
+        const int64_t start_sg = base + static_cast<int64_t>(g) * n;
+        const int64_t first = start_sg / Cw;
+        const int64_t last = (start_sg + n - 1) / Cw;
+        process(s, g, s_len[s], off, off + take, static_cast<int>(wr - first),
+                static_cast<int>(last - first + 1));
+        pos += take;
+        while (s < B && pos >= static_cast<int64_t>(H) * s_cum[s + 1]) ++s;
     }
 }
 
-// One workgroup per (sequence, query head): merge the partitions of a
-// sequence that has more than one.  With M the largest partition max, each
-// partition's sum and output are weighted by 2^(m_p - M); the result is their
-// ratio.  Thread t owns channel t % D and the partitions p = t / D (mod 256/D);
-// the partial sums are combined through LDS in a fixed order, so the result
-// does not depend on timing.
+// One workgroup per (sequence, query head): merge the partitions of a head
+// that has more than one.  With M the largest partition max, each partition's
+// sum and output are weighted by 2^(m_p - M); the result is their ratio.
+// Thread t owns channel t % D and the partitions p = t / D (mod 256/D); the
+// partial sums are combined through LDS in a fixed order, so the result does
+// not depend on timing.
 __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
@@ -398,17 +552,13 @@ __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) 
 }
 
 __global__ __launch_bounds__(256) void decode_reduce_kernel(void* out, int out_bf16,
-                                                           const int32_t* __restrict__ lens,
                                                            const float* __restrict__ ws_acc,
-                                                           const float2* __restrict__ ws_ml, int32_t B,
-                                                           int32_t Hq, int32_t D, int32_t max_ctx,
-                                                           int32_t part, int32_t P) {
+                                                           const float2* __restrict__ ws_ml,
+                                                           const int32_t* __restrict__ ws_np, int32_t D,
+                                                           int32_t P) {
     const int pair = blockIdx.x;
-    const int s = pair / Hq;
-    const int L = lens[s];
-    if (L < 1 || L > max_ctx) return;                       // the partition kernel wrote NaN
-    const int np = (L + part - 1) / part;
-    if (np <= 1) return;                                    // already final
+    const int np = min(ws_np[pair], P);
+    if (np <= 1) return;                                    // final already, or NaN written
     __shared__ float red[4];
     __shared__ float s_part[256];
     const int tid = threadIdx.x;
@@ -442,9 +592,9 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(void* out, int out_b
     s_part[tid] = o0 + o1;
     __syncthreads();
     if (grp == 0) {
-        float o = s_part[d];
-        for (int g2 = 1; g2 < groups; ++g2) o += s_part[g2 * D + d];
-        const float v = o / den;
+        float acc = s_part[d];
+        for (int g2 = 1; g2 < groups; ++g2) acc += s_part[g2 * D + d];
+        const float v = acc / den;
         const int64_t idx = static_cast<int64_t>(pair) * D + d;
         if (out_bf16)
             static_cast<__bf16*>(out)[idx] = static_cast<__bf16>(v);
@@ -453,15 +603,36 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(void* out, int out_b
     }
 }
 
-struct Checked {
-    int32_t part;
-    int32_t P;
+// ---- host side ----------------------------------------------------------------------
+struct Plan {
+    int32_t part_chunks;   // 0 = balanced
+    int32_t pmax;          // piece slots per (sequence, head); <= 1 means no workspace
     int32_t G;
 };
 
+// Piece slots per (sequence, head): fixed partitions need ceil(max_ctx / P);
+// a balanced range of >= kMinPieceChunks chunks cuts a head of n chunks into
+// at most ceil(n / kMinPieceChunks) + 1 pieces.
+int32_t piece_slots(int32_t max_context_len, int32_t part_chunks) {
+    const int64_t nch = (static_cast<int64_t>(max_context_len) + kChunk - 1) / kChunk;
+    if (part_chunks > 0) return static_cast<int32_t>((nch + part_chunks - 1) / part_chunks);
+    return static_cast<int32_t>((nch + kMinPieceChunks - 1) / kMinPieceChunks + 1);
+}
+
+int plan_partition(int32_t partition_size, int32_t* part_chunks) {
+    if (partition_size == 0) {
+        *part_chunks = 0;
+        return PA_OK;
+    }
+    if (partition_size < kChunk || partition_size % kChunk || partition_size > (1 << 20))
+        return PA_ERR_UNSUPPORTED;
+    *part_chunks = partition_size / kChunk;
+    return PA_OK;
+}
+
 int check_decode(const pa_cache_desc* desc, int32_t out_dtype, int32_t num_seqs, int32_t num_q_heads,
                  int32_t max_blocks_per_seq, int32_t max_context_len, int32_t partition_size,
-                 Checked* c) {
+                 Plan* c) {
     if (!desc_ok(desc) || num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq < 0 ||
         max_context_len < 1)
         return PA_ERR_INVALID_ARG;
@@ -469,36 +640,108 @@ int check_decode(const pa_cache_desc* desc, int32_t out_dtype, int32_t num_seqs,
     const int32_t H = desc->num_kv_heads;
     if (num_q_heads % H) return PA_ERR_INVALID_ARG;
     const int32_t G = num_q_heads / H;
-    const int32_t part = partition_size == 0 ? 512 : partition_size;
-    if (part < 128 || part > 512 || part % 128) return PA_ERR_UNSUPPORTED;
+    int rc = plan_partition(partition_size, &c->part_chunks);
+    if (rc != PA_OK) return rc;
     const int32_t bs = desc->block_size;
-    if (!is_pow2(bs) || bs < 8 || bs > part) return PA_ERR_UNSUPPORTED;
+    if (!is_pow2(bs) || bs < kMinBlock || bs > 256) return PA_ERR_UNSUPPORTED;
     if (G > 16) return PA_ERR_UNSUPPORTED;
     if (desc->head_dim != 64 && desc->head_dim != 128) return PA_ERR_UNSUPPORTED;
     if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * bs)
         return PA_ERR_INVALID_ARG;
-    c->part = part;
-    c->P = (max_context_len + part - 1) / part;
+    c->pmax = piece_slots(max_context_len, c->part_chunks);
     c->G = G;
     return PA_OK;
 }
 
-size_t workspace_bytes(int64_t B, int64_t Hq, int64_t D, int64_t P) {
-    if (P <= 1) return 0;
-    const int64_t acc = B * Hq * P * D * 4;
-    const int64_t acc_aligned = (acc + 255) / 256 * 256;
-    return static_cast<size_t>(acc_aligned + B * Hq * P * 8);
+// Workspace: the partials [B][Hq][pmax][D], their (max, sum) pairs
+// [B][Hq][pmax] and the piece count of every (sequence, head) [B][Hq].  None
+// is needed when every context fits one fixed partition.
+struct WsLayout {
+    size_t acc, ml, np, total;   // byte offsets of the three arrays and the total size
+};
+
+WsLayout workspace_layout(int64_t B, int64_t Hq, int64_t D, int64_t pmax, bool fixed) {
+    WsLayout l{0, 0, 0, 0};
+    if (fixed && pmax <= 1) return l;
+    auto al = [](int64_t x) { return (x + 255) / 256 * 256; };
+    l.acc = 0;
+    l.ml = static_cast<size_t>(al(B * Hq * pmax * D * 4));
+    l.np = l.ml + static_cast<size_t>(al(B * Hq * pmax * 8));
+    l.total = l.np + static_cast<size_t>(B * Hq * 4);
+    return l;
+}
+
+size_t decode_lds_bytes(int32_t nseq, int32_t G, int32_t D, bool fixed) {
+    return (fixed ? 0 : static_cast<size_t>(2 * nseq + 1) * sizeof(int)) +
+           static_cast<size_t>(kWaves) * G * (D + 4) * sizeof(float);
+}
+
+// Compute units of the current device (cached per device).
+int device_cus(int* cus) {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    int rc = hip_status(hipGetDevice(&dev));
+    if (rc != PA_OK) return rc;
+    if (dev >= 0 && dev < 64) {
+        const int n = cache[dev].load(std::memory_order_relaxed);
+        if (n > 0) {
+            *cus = n;
+            return PA_OK;
+        }
+    }
+    int n = 0;
+    rc = hip_status(hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev));
+    if (rc != PA_OK) return rc;
+    if (n <= 0) return PA_ERR_HIP;
+    if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    *cus = n;
+    return PA_OK;
 }
 
 template <bool BF16, int D>
-int launch_partitions_nch(int nch, dim3 grid, size_t lds, hipStream_t st, const DecodeArgs& a) {
-    switch (nch) {
-        case 1: return launch_kernel(decode_partition_kernel<BF16, D, 1>, grid, dim3(kThreads), lds, st, a);
-        case 2: return launch_kernel(decode_partition_kernel<BF16, D, 2>, grid, dim3(kThreads), lds, st, a);
-        case 3: return launch_kernel(decode_partition_kernel<BF16, D, 3>, grid, dim3(kThreads), lds, st, a);
-        case 4: return launch_kernel(decode_partition_kernel<BF16, D, 4>, grid, dim3(kThreads), lds, st, a);
-        default: return PA_ERR_UNSUPPORTED;
+int launch_partitions(const DecodeArgs& a0, int32_t num_seqs, const Plan& c, hipStream_t st) {
+    const auto kernel = decode_partition_kernel<BF16, D>;
+    int cus = 0;
+    int rc = device_cus(&cus);
+    if (rc != PA_OK) return rc;
+    constexpr int ES = BF16 ? 2 : 4;
+    const size_t per_seq_acc = static_cast<size_t>(a0.Hq) * c.pmax * D * 4;
+    const size_t per_seq_ml = static_cast<size_t>(a0.Hq) * c.pmax * 8;
+    for (int32_t s0 = 0; s0 < num_seqs; s0 += kMaxSeqsPerLaunch) {
+        const int32_t nb = std::min(kMaxSeqsPerLaunch, num_seqs - s0);
+        DecodeArgs a = a0;
+        a.B = nb;
+        a.out = static_cast<char*>(a0.out) + static_cast<int64_t>(s0) * a0.Hq * D * (a0.out_bf16 ? 2 : 4);
+        a.q = static_cast<const char*>(a0.q) + static_cast<int64_t>(s0) * a0.Hq * D * ES;
+        a.tables = a0.tables + static_cast<int64_t>(s0) * a0.maxb;
+        a.lens = a0.lens + s0;
+        if (a0.ws_np) {
+            a.ws_acc = reinterpret_cast<float*>(reinterpret_cast<char*>(a0.ws_acc) + s0 * per_seq_acc);
+            a.ws_ml = reinterpret_cast<float2*>(reinterpret_cast<char*>(a0.ws_ml) + s0 * per_seq_ml);
+            a.ws_np = a0.ws_np + static_cast<int64_t>(s0) * a0.Hq;
+        }
+        const bool fixed = c.part_chunks > 0;
+        const size_t lds = decode_lds_bytes(nb, c.G, D, fixed);
+        int64_t grid;
+        if (fixed) {
+            // one workgroup per (sequence, kv head, partition slot)
+            grid = static_cast<int64_t>(nb) * a.H * c.pmax;
+            if (grid > INT32_MAX) return PA_ERR_UNSUPPORTED;
+        } else {
+            // as many workgroups as the chip holds at once, and no more than
+            // minimal ranges of the longest context could keep busy
+            int per_cu = 0;
+            rc = hip_status(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, lds));
+            if (rc != PA_OK) return rc;
+            if (per_cu < 1) return PA_ERR_UNSUPPORTED;
+            const int64_t nch = (static_cast<int64_t>(a.max_ctx) + kChunk - 1) / kChunk;
+            const int64_t items = static_cast<int64_t>(nb) * a.H * ((nch + kMinPieceChunks - 1) / kMinPieceChunks);
+            grid = std::max<int64_t>(1, std::min<int64_t>(static_cast<int64_t>(per_cu) * cus, items));
+        }
+        rc = launch_kernel(kernel, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), lds, st, a);
+        if (rc != PA_OK) return rc;
     }
+    return PA_OK;
 }
 
 }  // namespace
@@ -508,10 +751,12 @@ extern "C" {
 
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                  int32_t max_context_len, int32_t partition_size) {
-    const int32_t part = partition_size == 0 ? 512 : partition_size;
-    if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 1 || part <= 0) return 0;
-    const int64_t P = (static_cast<int64_t>(max_context_len) + part - 1) / part;
-    return pa::workspace_bytes(num_seqs, num_q_heads, head_dim, P);
+    int32_t part_chunks = 0;
+    if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 1 ||
+        pa::plan_partition(partition_size, &part_chunks) != PA_OK)
+        return 0;
+    const int32_t pmax = pa::piece_slots(max_context_len, part_chunks);
+    return pa::workspace_layout(num_seqs, num_q_heads, head_dim, pmax, part_chunks > 0).total;
 }
 
 int pa_decode_partitions(void* out, int32_t out_dtype, const void* q, const void* k_cache,
@@ -521,17 +766,16 @@ int pa_decode_partitions(void* out, int32_t out_dtype, const void* q, const void
                          int32_t max_context_len, float scale, int32_t partition_size,
                          void* workspace, size_t workspace_bytes, void* stream) {
     using namespace pa;
-    Checked c;
+    Plan c;
     int rc = check_decode(desc, out_dtype, num_seqs, num_q_heads, max_blocks_per_seq, max_context_len,
                           partition_size, &c);
     if (rc != PA_OK) return rc;
     if (num_seqs == 0) return PA_OK;
     if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
     const int32_t D = desc->head_dim;
-    const size_t need = pa::workspace_bytes(num_seqs, num_q_heads, D, c.P);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_INVALID_ARG;
-    const int64_t units = static_cast<int64_t>(num_seqs) * desc->num_kv_heads * c.P;
-    if (units > INT32_MAX) return PA_ERR_UNSUPPORTED;
+    const WsLayout ws = workspace_layout(num_seqs, num_q_heads, D, c.pmax, c.part_chunks > 0);
+    if (ws.total > 0 && (!workspace || workspace_bytes < ws.total || reinterpret_cast<uintptr_t>(workspace) % 8))
+        return PA_ERR_INVALID_ARG;
 
     DecodeArgs a;
     a.out = out;
@@ -540,10 +784,10 @@ int pa_decode_partitions(void* out, int32_t out_dtype, const void* q, const void
     a.vc = v_cache;
     a.tables = block_tables;
     a.lens = context_lens;
-    const int64_t acc_bytes = static_cast<int64_t>(num_seqs) * num_q_heads * c.P * D * 4;
-    a.ws_acc = static_cast<float*>(workspace);
-    a.ws_ml = need ? reinterpret_cast<float2*>(static_cast<char*>(workspace) + (acc_bytes + 255) / 256 * 256)
-                   : nullptr;
+    char* wsb = static_cast<char*>(workspace);
+    a.ws_acc = ws.total ? reinterpret_cast<float*>(wsb + ws.acc) : nullptr;
+    a.ws_ml = ws.total ? reinterpret_cast<float2*>(wsb + ws.ml) : nullptr;
+    a.ws_np = ws.total ? reinterpret_cast<int32_t*>(wsb + ws.np) : nullptr;
     a.B = num_seqs;
     a.Hq = num_q_heads;
     a.H = desc->num_kv_heads;
@@ -552,43 +796,42 @@ int pa_decode_partitions(void* out, int32_t out_dtype, const void* q, const void
     a.N = desc->num_blocks;
     a.maxb = max_blocks_per_seq;
     a.max_ctx = max_context_len;
-    a.P = c.P;
+    a.part_chunks = c.part_chunks;
+    a.pmax = c.pmax;
     a.scale_log2 = scale * kLog2e;
     a.out_bf16 = out_dtype == PA_BF16;
 
-    const dim3 grid(static_cast<uint32_t>(units));
-    const size_t lds = static_cast<size_t>(kWaves) * c.G * (D + 4) * sizeof(float);
-    const int nch = c.part / (kChunk * kWaves);
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (desc->kv_dtype == PA_BF16)
-        return D == 128 ? launch_partitions_nch<true, 128>(nch, grid, lds, st, a)
-                        : launch_partitions_nch<true, 64>(nch, grid, lds, st, a);
-    return D == 128 ? launch_partitions_nch<false, 128>(nch, grid, lds, st, a)
-                    : launch_partitions_nch<false, 64>(nch, grid, lds, st, a);
+        return D == 128 ? launch_partitions<true, 128>(a, num_seqs, c, st)
+                        : launch_partitions<true, 64>(a, num_seqs, c, st);
+    return D == 128 ? launch_partitions<false, 128>(a, num_seqs, c, st)
+                    : launch_partitions<false, 64>(a, num_seqs, c, st);
 }
 
 int pa_decode_reduce(void* out, int32_t out_dtype, const int32_t* context_lens, int32_t num_seqs,
                      int32_t num_q_heads, int32_t head_dim, int32_t max_context_len,
                      int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
     using namespace pa;
-    if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 1) return PA_ERR_INVALID_ARG;
+    (void)context_lens;
+    if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 1) return PA_ERR_INVALID_ARG;
+    if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
     if (out_dtype != PA_F32 && out_dtype != PA_BF16) return PA_ERR_INVALID_ARG;
-    const int32_t part = partition_size == 0 ? 512 : partition_size;
-    if (part < 128 || part > 512 || part % 128) return PA_ERR_UNSUPPORTED;
-    const int32_t P = (max_context_len + part - 1) / part;
-    const size_t need = pa::workspace_bytes(num_seqs, num_q_heads, head_dim, P);
-    if (need == 0 || num_seqs == 0) return PA_OK;        // every sequence fits one partition
-    if (!out || !context_lens || !workspace || workspace_bytes < need) return PA_ERR_INVALID_ARG;
-    const int64_t pairs = static_cast<int64_t>(num_seqs) * num_q_heads;
-    const int64_t acc_bytes = pairs * P * head_dim * 4;
-    const float* ws_acc = static_cast<const float*>(workspace);
-    const float2* ws_ml =
-        reinterpret_cast<const float2*>(static_cast<const char*>(workspace) + (acc_bytes + 255) / 256 * 256);
-    const int64_t grid = pairs;
+    int32_t part_chunks = 0;
+    int rc = plan_partition(partition_size, &part_chunks);
+    if (rc != PA_OK) return rc;
+    const int32_t pmax = piece_slots(max_context_len, part_chunks);
+    const WsLayout ws = workspace_layout(num_seqs, num_q_heads, head_dim, pmax, part_chunks > 0);
+    if (ws.total == 0 || num_seqs == 0) return PA_OK;    // every head is a single partition
+    if (!out || !workspace || workspace_bytes < ws.total) return PA_ERR_INVALID_ARG;
+    const char* wsb = static_cast<const char*>(workspace);
+    const int64_t grid = static_cast<int64_t>(num_seqs) * num_q_heads;
     if (grid > INT32_MAX) return PA_ERR_UNSUPPORTED;
     return launch_kernel(decode_reduce_kernel, dim3(static_cast<uint32_t>(grid)), dim3(256), 0,
-                         static_cast<hipStream_t>(stream), out, out_dtype == PA_BF16, context_lens,
-                         ws_acc, ws_ml, num_seqs, num_q_heads, head_dim, max_context_len, part, P);
+                         static_cast<hipStream_t>(stream), out, out_dtype == PA_BF16,
+                         reinterpret_cast<const float*>(wsb + ws.acc),
+                         reinterpret_cast<const float2*>(wsb + ws.ml),
+                         reinterpret_cast<const int32_t*>(wsb + ws.np), head_dim, pmax);
 }
 
 int pa_decode(void* out, int32_t out_dtype, const void* q, const void* k_cache, const void* v_cache,

@@ -246,5 +246,13 @@ def test_device_calls_reject_bad_host_arguments():
     # a multi-partition launch without a workspace
     assert dec(one, 0, one, one, one, ref(desc), one, 64, one, 2, 8, 1000, 0.1, 0, None, 0, None) == pa.PA_ERR_INVALID_ARG
     assert dec(one, 7, one, one, one, ref(desc), one, 4, one, 2, 8, 64, 0.1, 0, None, 0, None) == pa.PA_ERR_INVALID_ARG
-    assert pa.pa_decode_workspace_bytes(2, 8, 128, 512) == 0
-    assert pa.pa_decode_workspace_bytes(2, 8, 128, 513) > 2 * 8 * 2 * 128 * 4
+    # fixed partitions: none needed while every context fits one partition
+    assert pa.pa_decode_workspace_bytes(2, 8, 128, 512, 512) == 0
+    assert pa.pa_decode_workspace_bytes(2, 8, 128, 513, 512) > 2 * 8 * 2 * 128 * 4
+    # balanced split (partition 0): a head of n 32-token chunks may be cut into
+    # ceil(n / 4) + 1 pieces, each holding D floats and a (max, sum) pair
+    pieces = -(-(-(-1000 // 32)) // 4) + 1
+    assert pa.pa_decode_workspace_bytes(2, 8, 128, 1000) >= 2 * 8 * pieces * (128 * 4 + 8) + 2 * 8 * 4
+    # partition sizes must be multiples of 32 tokens
+    assert pa.pa_decode_workspace_bytes(2, 8, 128, 1000, 100) == 0
+    assert dec(one, 0, one, one, one, ref(desc), one, 4, one, 2, 8, 64, 0.1, 48, None, 0, None) == pa.PA_ERR_UNSUPPORTED

@@ -21,7 +21,7 @@ def _announce(msg):
     print(f"[gpu-case] {msg}", flush=True)
 
 
-@pytest.mark.parametrize("name,part", [("c2", 512), ("c3", 256), ("c1", 128)])
+@pytest.mark.parametrize("name,part", [("c2", 0), ("c2", 512), ("c3", 256), ("c1", 128)])
 def test_decode_graph_replays_match_eager(name, part):
     _announce(f"graph decode {name} part {part}")
     w = workloads.make(name, small=True)
