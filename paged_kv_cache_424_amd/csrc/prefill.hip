@@ -9,23 +9,31 @@
 // positions 0 .. L - C + i.
 //
 // Work decomposition.  One workgroup (4 waves) per (chunk, kv head, tile of
-// 256 rows), a row being one (query position, query head of the kv head's
-// group): 256/G positions x G heads.  The workgroup walks the key positions in
-// tiles of 32; each tile's K rows and V channel rows are copied from their
-// physical blocks into LDS (double buffered, one barrier per tile) and shared
-// by the four waves.  Each wave owns 64 rows (four 16-row MFMA column tiles),
-// holds their query fragments in registers for the whole walk, and keeps an
-// online softmax per row.
+// 128 rows), a row being one (query position, query head of the kv head's
+// group): 128/G positions x G heads.  Each wave owns 32 rows -- one 32-row
+// column of a 32x32 MFMA tile -- and keeps their query fragments in registers
+// for the whole walk.  The workgroup walks the key positions in tiles of 64.
+// Each tile's K rows and V channel rows are copied from their physical blocks
+// into LDS one tile ahead (the loads for tile t+1 are in flight while tile t
+// is consumed, double-buffered LDS, one barrier per tile), and the block ids
+// two tiles ahead, so no table lookup sits on the critical path.  Two
+// workgroups share a CU and their barriers are independent, so one's softmax
+// overlaps the other's matrix work.
 //
-// Matrix cores, as in the decode kernel: S^T[key][row] = K . Q^T and
-// O^T[channel][row] += V^T . P^T with v_mfma_f32_16x16x32_bf16, so a lane's
-// softmax weights (row n, keys 8j..8j+7 of the tile) are exactly its operand
-// for the value MFMA and the per-row rescale is lane-local.  Weights enter
-// the value MFMA as bf16 (8-bit mantissa; the accumulation is fp32).  Per
-// 32-key tile a wave issues 64 MFMAs (16 cycles each) against 16 KB of LDS
-// reads, so the matrix cores, not LDS or HBM, set the pace.  LDS rows are
-// padded by 16 bytes so the 16 lanes of a quarter-wave read 16 different
-// bank groups.
+// Matrix cores: S^T[key][row] = K . Q^T and O^T[channel][row] += V^T . P^T with
+// v_mfma_f32_32x32x16_bf16.  In a 32x32 output a lane holds 16 rows of one
+// column, so a lane owns one query row: its softmax statistics need one
+// cross-lane step (the two halves of the wave), and its rescale and final
+// normalisation are lane-local.  The K rows of each 32-key MFMA tile are read
+// in a permuted order so that the logits a lane receives are exactly the
+// weights it must supply, as the value MFMA's B operand, for keys
+// 16 kb + 8 h .. +7 (h = lane / 32).  Weights enter the value MFMA as bf16
+// (8-bit mantissa, fp32 accumulation).  The running maximum is raised lazily:
+// only when a tile's maximum exceeds it by more than 2^8 in weight, so the
+// accumulator is rescaled a few times per row rather than per tile; weights
+// stay below 2^8, exact in the fp32 sums.  LDS rows are padded (K rows by
+// 16 bytes, V rows by 16 bytes) so that each quarter-wave's 16-byte reads hit
+// 16 different bank groups.
 
 #include "pa_internal.h"
 
@@ -34,19 +42,23 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kKeys = 32;                 // keys per tile
-constexpr int kNT = 4;                    // 16-row column tiles per wave
-constexpr int kRows = 16 * kNT * kWaves;  // 256 rows per workgroup
+constexpr int kRows = 32 * kWaves;        // 128 rows per workgroup
+constexpr int kKT = 64;                   // keys per tile
 constexpr int kD = 128;
-constexpr int kMT = kD / 16;              // channel tiles of the output
-constexpr int kKS = kD / 32;              // k-steps of the logits MFMA
+constexpr int kKS = kD / 16;              // k-steps of the logits MFMA (16 channels each)
+constexpr int kMT = kD / 32;              // 32-channel tiles of the output
+constexpr int kKB = kKT / 16;             // 16-key blocks of the value MFMA
 constexpr int kKStride = kD + 8;          // bf16 per K row in LDS (272 bytes)
-constexpr int kVStride = kKeys + 8;       // bf16 per V channel row in LDS (80 bytes)
+constexpr int kVStride = kKT + 8;         // bf16 per V channel row in LDS (144 bytes)
+constexpr int kMinBlock = 8;
+constexpr int kIdsPerTile = kKT / kMinBlock;   // block ids one tile can touch
+constexpr float kLazyLog2 = 8.f;          // raise the running max only when it grows by > 2^8
 
 struct PrefillArgs {
     void* out;
@@ -75,10 +87,19 @@ __device__ __forceinline__ u32x4 keep_first_bf16(u32x4 v, int n) {
 
 constexpr u32x4 kZero4 = {0u, 0u, 0u, 0u};
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void prefill_kernel(
+// Key (within a 32-key MFMA tile) whose K row feeds A-operand row r: rows
+// r = 8j + 4h + i take key 16 (j / 2) + 8 h + 4 (j % 2) + i, so that output
+// element e of lane (h = lane / 32) holds key 16 (e / 8) + 8 h + e % 8.
+__device__ __forceinline__ int k_row_key(int r) {
+    const int j = r >> 3, h = (r >> 2) & 1, i = r & 3;
+    return 16 * (j >> 1) + 8 * h + 4 * (j & 1) + i;
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(
     PrefillArgs a) {
-    __shared__ __align__(16) uint16_t sK[2][kKeys * kKStride];
+    __shared__ __align__(16) uint16_t sK[2][kKT * kKStride];
     __shared__ __align__(16) uint16_t sV[2][kD * kVStride];
+    __shared__ int s_ids[2][kIdsPerTile];
 
     const int u = xcd_remap(blockIdx.x, gridDim.x);
     const int qt = a.nqt - 1 - (u % a.nqt);       // longest query tiles of a chunk first
@@ -90,8 +111,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int n = lane & 15;
-    const int j = lane >> 4;
+    const int col = lane & 31;                    // this lane's row within the wave's 32
+    const int hh = lane >> 5;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
     const int qs0 = a.qsl[c];
@@ -119,34 +140,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     if (qt * QT >= Cc) return;
     const int P0 = Lc - Cc;                                    // position of query 0
     const int qhi = min(Cc, (qt + 1) * QT);                    // queries [qt*QT, qhi)
-    const int nkt = (P0 + qhi + kKeys - 1) / kKeys;            // key tiles to visit
+    const int nkt = (P0 + qhi + kKT - 1) / kKT;                // key tiles to visit
 
-    // ---- query fragments: lane (j, n) of column tile nt holds row 64w + 16nt + n ----
-    u32x4 qf[kNT][kKS];
-    int rowpos[kNT];                                           // absolute position of the row
-    bool rowok[kNT];
-#pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) {
-        const int rho = 64 * w + 16 * nt + n;
-        const int qi = qt * QT + (rho >> a.log2G);
-        const int h = rho & (G - 1);
-        rowok[nt] = qi < Cc;
-        rowpos[nt] = P0 + qi;
-        const uint16_t* qrow = a.q + (static_cast<int64_t>(qs0 + (rowok[nt] ? qi : 0)) * a.Hq + g * G + h) * kD;
+    // ---- this lane's row and its query fragments (B operand, k-step ks) ----
+    const int rho = 32 * w + col;
+    const int qi = qt * QT + (rho >> a.log2G);
+    const bool rowok = qi < Cc;
+    const int rowpos = P0 + qi;                                // absolute position of the row
+    u32x4 qf[kKS];
+    {
+        const uint16_t* qrow =
+            a.q + (static_cast<int64_t>(qs0 + (rowok ? qi : 0)) * a.Hq + g * G + (rho & (G - 1))) * kD;
 #pragma unroll
         for (int ks = 0; ks < kKS; ++ks) {
-            const u32x4 x = *reinterpret_cast<const u32x4*>(qrow + ks * 32 + j * 8);
-            qf[nt][ks] = rowok[nt] ? x : kZero4;
+            const u32x4 x = *reinterpret_cast<const u32x4*>(qrow + 16 * ks + 8 * hh);
+            qf[ks] = rowok ? x : kZero4;
         }
     }
 
-    // ---- tile loader: each thread moves 2 K segments and 2 V segments of 16 bytes ----
-    const int64_t tile_elems = static_cast<int64_t>(a.H) * a.bs * kD;
+    // ---- block ids: tile t touches blocks (64 t) / bs + [0, n_ids) ----
+    const int bs = a.bs;
+    const int n_ids = bs >= kKT ? 1 : kKT / bs;
+    const int nblk = (Lc + bs - 1) / bs;
     const int32_t* trow = a.tables + static_cast<int64_t>(c) * a.maxb;
-    const int nblk = (Lc + a.bs - 1) / a.bs;
     int bad = 0;
-    auto block_of = [&](int key) -> int64_t {
-        const int b = key / a.bs;
+    auto block_id = [&](int t, int i) -> int {
+        const int b = (t * kKT) / bs + i;
         if (b >= nblk) return 0;                 // past the context: any valid block, masked later
         const int id = trow[b];
         if (id < 0 || id >= a.N) {
@@ -155,140 +174,153 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         }
         return id;
     };
-    u32x4 pk[2], pv[2];
-    auto load_tile = [&](int kt) {
-        const int base = kt * kKeys;
+
+    // ---- tile loader: each thread moves 4 K segments and 4 V segments of 16 bytes ----
+    const int64_t tile_elems = static_cast<int64_t>(a.H) * bs * kD;
+    u32x4 pk[4], pv[4];
+    auto load_tile = [&](int t, const int* ids) {
+        const int base = t * kKT;
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
+        for (int p = 0; p < 4; ++p) {
             const int key = (tid >> 4) + 16 * p, seg = tid & 15;
-            const int kk = base + key;
-            const int64_t blk = block_of(kk);
+            const int x = base + key;
+            const int64_t blk = ids[bs >= kKT ? 0 : key / bs];
             pk[p] = *reinterpret_cast<const u32x4*>(
-                a.kc + ((blk * tile_elems) + (static_cast<int64_t>(g) * a.bs + kk % a.bs) * kD) + seg * 8);
+                a.kc + blk * tile_elems + (static_cast<int64_t>(g) * bs + x % bs) * kD + seg * 8);
         }
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int d = (tid >> 2) + 64 * p, sg = tid & 3;
-            const int kk0 = base + 8 * sg;
-            const int64_t blk = block_of(kk0);
-            const u32x4 x = *reinterpret_cast<const u32x4*>(
-                a.vc + (blk * tile_elems + (static_cast<int64_t>(g) * kD + d) * a.bs + kk0 % a.bs));
-            const int nval = Lc - kk0;                       // values past the context are zeroed
-            pv[p] = nval >= 8 ? x : keep_first_bf16(x, nval);
+        for (int p = 0; p < 4; ++p) {
+            const int d = (tid >> 3) + 32 * p, sg = tid & 7;
+            const int x0 = base + 8 * sg;
+            const int64_t blk = ids[bs >= kKT ? 0 : (8 * sg) / bs];
+            const u32x4 v = *reinterpret_cast<const u32x4*>(
+                a.vc + blk * tile_elems + (static_cast<int64_t>(g) * kD + d) * bs + x0 % bs);
+            const int nval = Lc - x0;                // values past the context are zeroed
+            pv[p] = nval >= 8 ? v : keep_first_bf16(v, nval);
         }
     };
     auto store_tile = [&](int buf) {
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
+        for (int p = 0; p < 4; ++p) {
             const int key = (tid >> 4) + 16 * p, seg = tid & 15;
             *reinterpret_cast<u32x4*>(&sK[buf][key * kKStride + seg * 8]) = pk[p];
         }
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int d = (tid >> 2) + 64 * p, sg = tid & 3;
+        for (int p = 0; p < 4; ++p) {
+            const int d = (tid >> 3) + 32 * p, sg = tid & 7;
             *reinterpret_cast<u32x4*>(&sV[buf][d * kVStride + 8 * sg]) = pv[p];
         }
     };
 
-    f32x4_t acc[kNT][kMT];
+    f32x16_t acc[kMT];
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt)
+    for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
-        for (int mt = 0; mt < kMT; ++mt) acc[nt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m_run[kNT], l_run[kNT];
-#pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) {
-        m_run[nt] = -INFINITY;
-        l_run[nt] = 0.f;
-    }
-    const int wave_min_pos = P0 + qt * QT + ((64 * w) >> a.log2G);   // smallest position of this wave's rows
+        for (int e = 0; e < 16; ++e) acc[mt][e] = 0.f;
+    float m_run = -INFINITY;                      // running max of the row's logits (raw units)
+    float l_run = 0.f;                            // this lane's half of the row's weight sum
+    const float cscale = a.scale_log2;
+    const float lazy = kLazyLog2 / cscale;        // max growth tolerated before a rescale (raw units)
+    const int wave_min_pos = P0 + qt * QT + ((32 * w) >> a.log2G);
+    const int krow0 = k_row_key(col);             // K row read for A-operand row `col`
 
-    load_tile(0);
+    // ---- prologue: ids of tiles 0 and 1, then tile 0 into LDS ----
+    if (tid < n_ids) {
+        s_ids[0][tid] = block_id(0, tid);
+        if (nkt > 1) s_ids[1][tid] = block_id(1, tid);
+    }
+    __syncthreads();
+    load_tile(0, s_ids[0]);
     store_tile(0);
     __syncthreads();
+
     for (int kt = 0; kt < nkt; ++kt) {
         const int buf = kt & 1;
-        const int base = kt * kKeys;
-        if (kt + 1 < nkt) load_tile(kt + 1);
+        const int base = kt * kKT;
+        if (kt + 1 < nkt) load_tile(kt + 1, s_ids[buf ^ 1]);
+        int nid = 0;
+        if (kt + 2 < nkt && tid < n_ids) nid = block_id(kt + 2, tid);
 
-        // ---- logits S^T[key][row]; key row r of tile t is key 8(r/4) + r%4 + 4t ----
-        f32x4_t st[2][kNT];
+        // ---- logits S^T[key][row] for the tile's two 32-key MFMA tiles ----
+        f32x16_t st[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const int krow = 8 * (n >> 2) + (n & 3) + 4 * t;
-            u32x4 kf[kKS];
+            f32x16_t s4;
 #pragma unroll
-            for (int ks = 0; ks < kKS; ++ks)
-                kf[ks] = *reinterpret_cast<const u32x4*>(&sK[buf][krow * kKStride + ks * 32 + j * 8]);
+            for (int e = 0; e < 16; ++e) s4[e] = 0.f;
+            const uint16_t* krow = &sK[buf][(32 * t + krow0) * kKStride + 8 * hh];
 #pragma unroll
-            for (int nt = 0; nt < kNT; ++nt) {
-                f32x4_t s4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < kKS; ++ks)
-                    s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[ks]), as_bf16x8(qf[nt][ks]), s4, 0, 0, 0);
-                st[t][nt] = s4;
+            for (int ks = 0; ks < kKS; ++ks) {
+                const u32x4 kf = *reinterpret_cast<const u32x4*>(krow + 16 * ks);
+                s4 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[ks]), s4, 0, 0, 0);
             }
+            st[t] = s4;
         }
-        // ---- online softmax per row; lane (j, n) holds keys base + 8j + e ----
-        const bool diag = base + kKeys - 1 > wave_min_pos;   // some key may lie after some row
-        bf16x8_t pb[kNT];
+        // element e of tile t holds key base + 32 t + 16 (e / 8) + 8 hh + e % 8
+        if (base + kKT - 1 > wave_min_pos) {
 #pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) {
-            float sv[8];
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float x = st[e >> 2][nt][e & 3] * a.scale_log2;
-                sv[e] = (!diag || base + 8 * j + e <= rowpos[nt]) ? x : -INFINITY;
-            }
-            float cm = sv[0];
-#pragma unroll
-            for (int e = 1; e < 8; ++e) cm = fmaxf(cm, sv[e]);
-            cm = fmaxf(cm, __shfl_xor(cm, 16));
-            cm = fmaxf(cm, __shfl_xor(cm, 32));
-            const float m_new = fmaxf(m_run[nt], cm);         // finite: key 0 <= every position
-            const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_new);
-            m_run[nt] = m_new;
-            float ps = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float pe = __builtin_amdgcn_exp2f(sv[e] - m_new);
-                ps += pe;
-                pb[nt][e] = static_cast<__bf16>(pe);
-            }
-            l_run[nt] = l_run[nt] * alpha + ps;
-            if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-                for (int mt = 0; mt < kMT; ++mt) acc[nt][mt] *= alpha;
-            }
+                for (int e = 0; e < 16; ++e) {
+                    const int key = base + 32 * t + 16 * (e >> 3) + 8 * hh + (e & 7);
+                    st[t][e] = key <= rowpos ? st[t][e] : -INFINITY;
+                }
         }
+        // ---- online softmax of the row (this lane and lane ^ 32 share it) ----
+        float mx = st[0][0];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, st[t][e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const bool grow = mx > m_run + lazy;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+            const float m_new = grow ? mx : m_run;
+            const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * cscale) : 1.f;
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int mt = 0; mt < kMT; ++mt) acc[mt] *= alpha;
+        }
+        const float neg_m = -m_run * cscale;
+        bf16x8_t pb[kKB];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float p = __builtin_amdgcn_exp2f(fmaf(st[t][e], cscale, neg_m));
+                l_run += p;
+                pb[2 * t + (e >> 3)][e & 7] = static_cast<__bf16>(p);
+            }
         // ---- values: O^T[channel][row] += V^T[channel][key] . P^T[key][row] ----
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) {
-            const u32x4 vf = *reinterpret_cast<const u32x4*>(&sV[buf][(mt * 16 + n) * kVStride + 8 * j]);
+            const uint16_t* vrow = &sV[buf][(32 * mt + col) * kVStride + 8 * hh];
 #pragma unroll
-            for (int nt = 0; nt < kNT; ++nt)
-                acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vf), pb[nt], acc[nt][mt], 0, 0, 0);
+            for (int kb = 0; kb < kKB; ++kb) {
+                const u32x4 vf = *reinterpret_cast<const u32x4*>(vrow + 16 * kb);
+                acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), pb[kb], acc[mt], 0, 0, 0);
+            }
         }
         if (kt + 1 < nkt) store_tile(buf ^ 1);
+        if (kt + 2 < nkt && tid < n_ids) s_ids[buf][tid] = nid;
         __syncthreads();
     }
     bad = __syncthreads_or(bad);
 
-    // ---- normalise and store: lane (j, n) holds channels mt*16 + 4j .. +3 of its row ----
+    // ---- normalise and store: lane holds channels 32 mt + 8 (e / 4) + 4 hh + e % 4 of its row ----
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    if (!rowok) return;
+    const int64_t orow = (static_cast<int64_t>(qs0 + qi) * a.Hq + g * G + (rho & (G - 1))) * kD;
+    const float inv = 1.f / l_tot;
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) {
-        float l = l_run[nt] + __shfl_xor(l_run[nt], 16);
-        l += __shfl_xor(l, 32);
-        if (!rowok[nt]) continue;
-        const int rho = 64 * w + 16 * nt + n;
-        const int qi = qt * QT + (rho >> a.log2G);
-        const int64_t orow = (static_cast<int64_t>(qs0 + qi) * a.Hq + g * G + (rho & (G - 1))) * kD;
-        const float inv = 1.f / l;
+    for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
-        for (int mt = 0; mt < kMT; ++mt) {
-            f32x4_t v = acc[nt][mt] * inv;
-            if (bad) v = f32x4_t{kNaN, kNaN, kNaN, kNaN};
-            const int64_t o = orow + mt * 16 + 4 * j;
+        for (int e4 = 0; e4 < 4; ++e4) {
+            f32x4_t v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = bad ? kNaN : acc[mt][4 * e4 + i] * inv;
+            const int64_t o = orow + 32 * mt + 8 * e4 + 4 * hh;
             if (a.out_bf16) {
                 __bf16* dst = static_cast<__bf16*>(a.out) + o;
 #pragma unroll
@@ -297,7 +329,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.out) + o) = v;
             }
         }
-    }
 }
 
 }  // namespace
@@ -318,7 +349,8 @@ extern "C" int pa_prefill(void* out, int32_t out_dtype, const void* q, const voi
     const int32_t G = num_q_heads / H;
     if (desc->kv_dtype != PA_BF16 || desc->head_dim != kD) return PA_ERR_UNSUPPORTED;
     if (!is_pow2(G) || G > 16) return PA_ERR_UNSUPPORTED;
-    if (!is_pow2(desc->block_size) || desc->block_size < 8 || desc->block_size > 256) return PA_ERR_UNSUPPORTED;
+    if (!is_pow2(desc->block_size) || desc->block_size < kMinBlock || desc->block_size > 256)
+        return PA_ERR_UNSUPPORTED;
     if (num_chunks == 0 || max_query_len == 0 || num_query_tokens == 0) return PA_OK;
     if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start_loc)
         return PA_ERR_INVALID_ARG;
