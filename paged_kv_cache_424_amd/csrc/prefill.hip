@@ -10,9 +10,10 @@
 //
 // Work decomposition.  One workgroup (4 waves) per (chunk, kv head, tile of
 // 128 rows), a row being one (query position, query head of the kv head's
-// group): 128/G positions x G heads.  Each wave owns 32 rows -- one 32-row
-// column of a 32x32 MFMA tile -- and keeps their query fragments in registers
-// for the whole walk.  The workgroup walks the key positions in tiles of 64.
+// group): 128/G positions x G heads.  The (chunk, head) pairs are spread over
+// the eight XCDs and taken longest first (see the kernel's prologue).  Each
+// wave owns 32 rows -- one 32-row column of a 32x32 MFMA tile -- and keeps
+// their query fragments in registers for the whole walk.  The workgroup walks the key positions in tiles of 64.
 // Each tile's K rows and V channel rows are copied from their physical blocks
 // into LDS one tile ahead (the loads for tile t+1 are in flight while tile t
 // is consumed, double-buffered LDS, one barrier per tile), and the block ids
@@ -59,6 +60,7 @@ constexpr int kVStride = kKT + 8;         // bf16 per V channel row in LDS (144 
 constexpr int kMinBlock = 8;
 constexpr int kIdsPerTile = kKT / kMinBlock;   // block ids one tile can touch
 constexpr float kLazyLog2 = 8.f;          // raise the running max only when it grows by > 2^8
+constexpr int kMaxSortedChunks = 256;     // chunks ranked by length inside the kernel
 
 struct PrefillArgs {
     void* out;
@@ -68,7 +70,7 @@ struct PrefillArgs {
     const int32_t* tables;
     const int32_t* lens;
     const int32_t* qsl;
-    int32_t num_chunks, Hq, H, G, log2G, bs, N, maxb, max_q, nqt, total_q;
+    int32_t num_chunks, Hq, H, G, log2G, bs, log2bs, N, maxb, max_q, nqt, total_q;
     float scale_log2;
     int32_t out_bf16;
 };
@@ -100,16 +102,42 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     __shared__ __align__(16) uint16_t sK[2][kKT * kKStride];
     __shared__ __align__(16) uint16_t sV[2][kD * kVStride];
     __shared__ int s_ids[2][kIdsPerTile];
+    __shared__ int s_order[kMaxSortedChunks];
 
-    const int u = xcd_remap(blockIdx.x, gridDim.x);
-    const int qt = a.nqt - 1 - (u % a.nqt);       // longest query tiles of a chunk first
-    const int cg = u / a.nqt;
-    const int g = cg % a.H;
-    const int c = cg / a.H;
+    // ---- which (chunk, kv head, query tile) this workgroup takes ----
+    // Workgroup b runs on XCD b % 8 (dispatch is round robin over the XCDs).
+    // The (chunk, kv head) pairs are dealt round robin to the XCDs, so every
+    // XCD gets a share of every chunk while the query tiles of one pair --
+    // which read the same K/V -- stay on one XCD and share its L2.  Within
+    // an XCD the work goes longest first: chunks by decreasing context
+    // length (ranked here from the lengths, when there are few enough
+    // chunks), query tiles of a chunk from the last one down.
+    const int tid = threadIdx.x;
+    const int nc = a.num_chunks;
+    if (nc <= kMaxSortedChunks) {
+        for (int i = tid; i < nc; i += kThreads) {
+            const int Li = a.lens[i];
+            int rank = 0;
+            for (int jc = 0; jc < nc; ++jc) {
+                const int Lj = a.lens[jc];
+                rank += (Lj > Li) || (Lj == Li && jc < i);
+            }
+            s_order[rank] = i;
+        }
+        __syncthreads();
+    }
+    const int xcd = blockIdx.x % kNumXcds;
+    const int k = blockIdx.x / kNumXcds;
+    const int npairs = nc * a.H;
+    const int npairs_x = (npairs - xcd + kNumXcds - 1) / kNumXcds;   // pairs xcd, xcd + 8, ...
+    if (k >= npairs_x * a.nqt) return;
+    const int pr = xcd + kNumXcds * (k / a.nqt);                      // pair in longest-first order
+    const int qt = a.nqt - 1 - (k % a.nqt);
+    const int g = pr % a.H;
+    const int c = nc <= kMaxSortedChunks ? s_order[pr / a.H] : pr / a.H;
     const int G = a.G;
     const int QT = kRows >> a.log2G;              // query positions per tile
 
-    const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int col = lane & 31;                    // this lane's row within the wave's 32
     const int hh = lane >> 5;
@@ -176,27 +204,46 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     };
 
     // ---- tile loader: each thread moves 4 K segments and 4 V segments of 16 bytes ----
-    const int64_t tile_elems = static_cast<int64_t>(a.H) * bs * kD;
+    // K segment p: key (tid / 16) + 16 p of the tile, channels 8 (tid % 16) ..
+    // +7.  V segment p: channel (tid / 8) + 32 p, keys 8 (tid % 8) .. +7 (one
+    // block, as block_size >= 8).  With block_size <= 64 a tile starts on a
+    // block boundary, so a segment's block slot and in-block offset are the
+    // same for every tile and are computed once here; larger blocks add the
+    // tile's offset inside its block.
+    const int log2bs = a.log2bs;
+    const bool big_blocks = bs > kKT;
+    const int64_t tile_bytes = static_cast<int64_t>(a.H) * bs * kD * 2;
+    const char* kbase = reinterpret_cast<const char*>(a.kc) + static_cast<int64_t>(g) * bs * kD * 2;
+    const char* vbase = reinterpret_cast<const char*>(a.vc) + static_cast<int64_t>(g) * kD * bs * 2;
+    int kslot[4], koff[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int key = (tid >> 4) + 16 * p;
+        kslot[p] = big_blocks ? 0 : key >> log2bs;
+        koff[p] = ((big_blocks ? key : key & (bs - 1)) * kD + (tid & 15) * 8) * 2;   // bytes
+    }
+    const int vkey = 8 * (tid & 7);
+    const int vslot = big_blocks ? 0 : vkey >> log2bs;
+    const int voff = (((tid >> 3) * bs) + (big_blocks ? vkey : vkey & (bs - 1))) * 2;  // bytes, p = 0
+    const int vstep = 32 * bs * 2;                                                   // bytes per p
     u32x4 pk[4], pv[4];
     auto load_tile = [&](int t, const int* ids) {
         const int base = t * kKT;
+        // the tile's offset inside its block (only for blocks larger than a tile)
+        const int in_blk = big_blocks ? (base & (bs - 1)) : 0;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            const int key = (tid >> 4) + 16 * p, seg = tid & 15;
-            const int x = base + key;
-            const int64_t blk = ids[bs >= kKT ? 0 : key / bs];
-            pk[p] = *reinterpret_cast<const u32x4*>(
-                a.kc + blk * tile_elems + (static_cast<int64_t>(g) * bs + x % bs) * kD + seg * 8);
+            const char* src = kbase + ids[kslot[p]] * tile_bytes + koff[p] + in_blk * kD * 2;
+            pk[p] = *reinterpret_cast<const u32x4*>(src);
         }
+        const char* vsrc = vbase + ids[vslot] * tile_bytes + voff + in_blk * 2;
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int d = (tid >> 3) + 32 * p, sg = tid & 7;
-            const int x0 = base + 8 * sg;
-            const int64_t blk = ids[bs >= kKT ? 0 : (8 * sg) / bs];
-            const u32x4 v = *reinterpret_cast<const u32x4*>(
-                a.vc + blk * tile_elems + (static_cast<int64_t>(g) * kD + d) * bs + x0 % bs);
-            const int nval = Lc - x0;                // values past the context are zeroed
-            pv[p] = nval >= 8 ? v : keep_first_bf16(v, nval);
+        for (int p = 0; p < 4; ++p) pv[p] = *reinterpret_cast<const u32x4*>(vsrc + p * vstep);
+        if (base + kKT > Lc) {
+            // values past the context are zeroed (a weight of 0 does not cancel a NaN)
+            const int nval = Lc - (base + vkey);
+#pragma unroll
+            for (int p = 0; p < 4; ++p) pv[p] = keep_first_bf16(pv[p], nval);
         }
     };
     auto store_tile = [&](int buf) {
@@ -211,7 +258,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             *reinterpret_cast<u32x4*>(&sV[buf][d * kVStride + 8 * sg]) = pv[p];
         }
     };
-
     f32x16_t acc[kMT];
 #pragma unroll
     for (int mt = 0; mt < kMT; ++mt)
@@ -283,23 +329,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             for (int mt = 0; mt < kMT; ++mt) acc[mt] *= alpha;
         }
         const float neg_m = -m_run * cscale;
-        bf16x8_t pb[kKB];
+        // Weights and values one 32-key half at a time: the value MFMAs of
+        // the first half are independent of the second half's exponentials,
+        // so the two overlap within the wave.
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < 2; ++t) {
+            bf16x8_t pb[2];
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const float p = __builtin_amdgcn_exp2f(fmaf(st[t][e], cscale, neg_m));
                 l_run += p;
-                pb[2 * t + (e >> 3)][e & 7] = static_cast<__bf16>(p);
+                pb[e >> 3][e & 7] = static_cast<__bf16>(p);
             }
-        // ---- values: O^T[channel][row] += V^T[channel][key] . P^T[key][row] ----
+            // ---- values: O^T[channel][row] += V^T[channel][key] . P^T[key][row] ----
 #pragma unroll
-        for (int mt = 0; mt < kMT; ++mt) {
-            const uint16_t* vrow = &sV[buf][(32 * mt + col) * kVStride + 8 * hh];
+            for (int mt = 0; mt < kMT; ++mt) {
+                const uint16_t* vrow = &sV[buf][(32 * mt + col) * kVStride + 8 * hh + 32 * t];
 #pragma unroll
-            for (int kb = 0; kb < kKB; ++kb) {
-                const u32x4 vf = *reinterpret_cast<const u32x4*>(vrow + 16 * kb);
-                acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), pb[kb], acc[mt], 0, 0, 0);
+                for (int kb = 0; kb < 2; ++kb) {
+                    const u32x4 vf = *reinterpret_cast<const u32x4*>(vrow + 16 * kb);
+                    acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), pb[kb], acc[mt], 0, 0, 0);
+                }
             }
         }
         if (kt + 1 < nkt) store_tile(buf ^ 1);
@@ -358,7 +408,10 @@ extern "C" int pa_prefill(void* out, int32_t out_dtype, const void* q, const voi
     while ((1 << log2G) < G) ++log2G;
     const int QT = kRows / G;
     const int64_t nqt = (max_query_len + QT - 1) / QT;
-    const int64_t units = static_cast<int64_t>(num_chunks) * H * nqt;
+    // every XCD gets the same number of workgroups: ceil(pairs / 8) pairs'
+    // worth; the surplus ones of the XCDs with a pair fewer exit at once
+    const int64_t pairs = static_cast<int64_t>(num_chunks) * H;
+    const int64_t units = kNumXcds * ((pairs + kNumXcds - 1) / kNumXcds) * nqt;
     if (units > INT32_MAX) return PA_ERR_UNSUPPORTED;
     PrefillArgs a;
     a.out = out;
@@ -374,6 +427,9 @@ extern "C" int pa_prefill(void* out, int32_t out_dtype, const void* q, const voi
     a.G = G;
     a.log2G = log2G;
     a.bs = desc->block_size;
+    int log2bs = 0;
+    while ((1 << log2bs) < a.bs) ++log2bs;
+    a.log2bs = log2bs;
     a.N = desc->num_blocks;
     a.maxb = max_blocks_per_seq;
     a.max_q = max_query_len;
