@@ -183,10 +183,13 @@ int pa_cache_write(void* k_cache, void* v_cache, const pa_cache_desc* desc, cons
 int pa_copy_blocks(void* k_cache, void* v_cache, const pa_cache_desc* desc,
                    const int64_t* pairs_host, int32_t n_pairs, void* stream);
 
-/* Workspace bytes pa_decode needs: room for the per-partition running max, sum
- * and unnormalised output of every (sequence, query head, partition) when a
- * sequence spans more than one partition; 0 when max_context_len fits in one.
- * partition_size 0 means 512. */
+/* Workspace bytes pa_decode needs: room for the running max, sum and
+ * unnormalised output of every piece of every (sequence, query head), plus one
+ * piece count per (sequence, query head).  With fixed partitions
+ * (partition_size > 0) a head has ceil(L / partition_size) pieces and no
+ * workspace is needed (0) while max_context_len fits one partition; with the
+ * balanced split (partition_size 0) a head of n 32-token chunks has at most
+ * ceil(n / 4) + 1 pieces.  0 also for invalid arguments. */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                  int32_t max_context_len, int32_t partition_size);
 
@@ -202,15 +205,23 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *                 ceil(L/block_size) entries of a row are read.
  *   context_lens: device int32 [num_seqs]; L counts the newest token.
  *   max_context_len: an upper bound of every L, used to size the grid.
- *   partition_size: tokens per split-K partition (0 = 512); a multiple of 128
- *                 and of block_size, at most 512.
- *   workspace:    device scratch of >= pa_decode_workspace_bytes(...) bytes, or
- *                 NULL when that is 0.
+ *   partition_size: 0 for the balanced split -- the 32-token chunks of all
+ *                 (sequence, kv head) pairs are cut into equal ranges, one per
+ *                 workgroup the chip holds at once, so the cut points (and the
+ *                 fp32 rounding order of a row) depend on the whole batch and
+ *                 the device's compute-unit count; or P > 0, a multiple of 32,
+ *                 for pieces at absolute positions 0, P, 2P, ..., which make a
+ *                 row's result depend on that row alone.
+ *   workspace:    device scratch of >= pa_decode_workspace_bytes(...) bytes
+ *                 (8-byte aligned), or NULL when that is 0.  Its contents
+ *                 before the call do not matter.  Calls that overlap in time
+ *                 must not share a workspace.
  * Device-side checks: a row whose L is < 1 or > max_context_len, whose needed
  * table entries leave [0, num_blocks), or whose L exceeds
  * max_blocks_per_seq*block_size, produces NaN outputs instead of reading out of
  * bounds.  Supported: head_dim 64 or 128, num_q_heads/num_kv_heads in 1..16,
- * block_size 8..256 a power of two (fp32 caches: 4..256), cache PA_F32 or PA_BF16.
+ * block_size 8..256 a power of two, cache PA_F32 or PA_BF16.  PA_ERR_UNSUPPORTED
+ * for anything else, and for a partition_size that is not a multiple of 32.
  * Runs pa_decode_partitions then pa_decode_reduce. */
 int pa_decode(void* out, int32_t out_dtype, const void* q, const void* k_cache,
               const void* v_cache, const pa_cache_desc* desc, const int32_t* block_tables,
@@ -218,9 +229,9 @@ int pa_decode(void* out, int32_t out_dtype, const void* q, const void* k_cache,
               int32_t num_q_heads, int32_t max_context_len, float scale, int32_t partition_size,
               void* workspace, size_t workspace_bytes, void* stream);
 
-/* First half of pa_decode: one workgroup per (sequence, kv head, partition).
- * Sequences with one partition get their final output written here; the
- * others leave per-partition partials in the workspace for pa_decode_reduce.
+/* First half of pa_decode: the split-K pass.  Heads whose context is a single
+ * piece get their final output written here; the others leave per-piece
+ * partials and their piece count in the workspace for pa_decode_reduce.
  * Same arguments and checks as pa_decode. */
 int pa_decode_partitions(void* out, int32_t out_dtype, const void* q, const void* k_cache,
                          const void* v_cache, const pa_cache_desc* desc,
@@ -229,9 +240,11 @@ int pa_decode_partitions(void* out, int32_t out_dtype, const void* q, const void
                          int32_t max_context_len, float scale, int32_t partition_size,
                          void* workspace, size_t workspace_bytes, void* stream);
 
-/* Second half of pa_decode: merge the partitions of every sequence that has
- * more than one, rescaling each partition's sum by exp(its max - overall max).
- * Arguments as in pa_decode (the same values must be passed to both halves). */
+/* Second half of pa_decode: merge the pieces of every (sequence, query head)
+ * that has more than one, rescaling each piece's sum and output by
+ * exp(its max - overall max).  Arguments as in pa_decode (the same values must
+ * be passed to both halves); context_lens is not read (the piece counts come
+ * from the workspace) and may be NULL. */
 int pa_decode_reduce(void* out, int32_t out_dtype, const int32_t* context_lens, int32_t num_seqs,
                      int32_t num_q_heads, int32_t head_dim, int32_t max_context_len,
                      int32_t partition_size, void* workspace, size_t workspace_bytes,
