@@ -191,6 +191,8 @@ def main():
                     help="split-K partition in tokens (a multiple of 32), or 0 for the balanced split; "
                          "default: 512 for the long-context workload (its stated partition), else 0")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the extra HIP-graph replay measurement of the whole step")
     ap.add_argument("--cpu-seqs", type=int, default=0, help="sequences in the oracle sample (0 = auto)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB elementwise kernel (scales the HBM byte counters)")
@@ -267,41 +269,80 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    def step(i, ev=None):
+    # Events: in the timed steps only around the partition kernel (2, 3) and
+    # the prefill kernel (4, 5), so that event records add no gaps elsewhere;
+    # a separate pass after the timed region records all of them: 0 start,
+    # 1 after copy_blocks, 2 after cache_write, 3 after the partition kernel,
+    # 4 after the reduce, 5 after prefill.
+    timed_marks = (2, 3, 4, 5) if pre is not None else (2, 3)
+
+    def step(i, ev=None, marks=timed_marks):
+        def mark(k):
+            if ev is not None and k in marks:
+                ev[k].record()
         kc, vc = pools[i % copies]
+        mark(0)
         if pairs:
             pa.pa_copy_blocks(kc, vc, st.desc, pairs)
+        mark(1)
         pa.pa_cache_write(kc, vc, st.desc, k_new, v_new, slots)
-        if ev is not None:
-            ev[0].record()
+        mark(2)
         pa.pa_decode_partitions(out, st.q, kc, vc, st.desc, st.tables, st.lens, max_ctx, w.scale,
                                 args.partition, ws)
-        if ev is not None:
-            ev[1].record()
+        mark(3)
         pa.pa_decode_reduce(out, st.lens, Hq, D, max_ctx, args.partition, ws)
+        mark(4)
         if pre is not None:
-            if ev is not None:
-                ev[2].record()
             pa.pa_prefill(pre["out"], pre["q"], kc, vc, st.desc, pre["tables"], pre["lens"], pre["qsl"],
                           pre["max_q"], w.scale)
-            if ev is not None:
-                ev[3].record()
+        mark(5)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(args.steps)]
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(6)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(args.warmup + i, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    part_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    part_ms = [e[2].elapsed_time(e[3]) for e in evs]
     part_avg_s = float(np.mean(part_ms)) / 1e3
     assert torch.isfinite(out).all()
 
     ms_per_step = wall * 1e3 / args.steps
+
+    # per-kernel times, all events recorded (not part of the timed region)
+    evk = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(6)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(args.warmup + i, evk[i], marks=(0, 1, 2, 3, 4, 5))
+    torch.cuda.synchronize()
+
+    def avg_us(a, b):
+        return float(np.mean([e[a].elapsed_time(e[b]) for e in evk])) * 1e3
+
+    # The same step captured once per pool copy as a HIP graph and replayed:
+    # the launch gaps between the step's kernels shrink.  Reported beside the
+    # eager figures (the timed region above), which carry the kernel's event
+    # timing -- events cannot be recorded inside a captured graph here.
+    graph_ms = None
+    if not args.no_graph:
+        graphs = []
+        for i in range(copies):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                step(i)
+            graphs.append(gr)
+        for i in range(copies):
+            graphs[i].replay()
+        torch.cuda.synchronize()
+        tg = time.perf_counter()
+        for i in range(args.steps):
+            graphs[i % copies].replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - tg) * 1e3 / args.steps
+        assert torch.isfinite(out).all()
     # algorithmic bytes of one decode: every context token's K and V of every kv
     # head once, the queries, the fp32 outputs, the block ids and lengths
     nblocks = int(np.sum(-(-lens // w.block_size)))
@@ -333,9 +374,13 @@ def main():
                      "p90_us": float(np.percentile(part_ms, 90)) * 1e3,
                      "kernel_source_hash": kernel_source_hash()},
         "decode_gbs_whole_step": algo / (ms_per_step / 1e3) / 1e9,
+        "hip_graph_ms_per_step": graph_ms,
+        "kernels_us_untimed_pass": {"copy_blocks": avg_us(0, 1) if pairs else None, "cache_write": avg_us(1, 2),
+                       "decode_partitions": avg_us(2, 3), "decode_reduce": avg_us(3, 4),
+                       "prefill": avg_us(4, 5) if pre is not None else None},
     }
     if pre is not None:
-        pre_ms = [e[2].elapsed_time(e[3]) for e in evs]
+        pre_ms = [e[4].elapsed_time(e[5]) for e in evs]
         pre_s = float(np.mean(pre_ms)) / 1e3
         tf = pre["flops"] / pre_s / 1e12
         assert torch.isfinite(pre["out"]).all()

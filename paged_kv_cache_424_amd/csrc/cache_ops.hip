@@ -7,43 +7,52 @@
 //   (Copy-on-Write): a shared block is duplicated before one sharer diverges.
 //
 // Both kernels move raw bits (16/32-bit integers), so every value -- NaN
-// payloads included -- arrives unchanged.  Both are HBM-latency bound at the
-// sizes a decode step writes; they exist to be correct and cheap to launch.
+// payloads included -- arrives unchanged.  At the sizes a decode step writes
+// they are bound by launch and HBM latency.
 
 #include "pa_internal.h"
 
 namespace pa {
 namespace {
 
-// One thread per 4-byte word of a token's K row (2 bf16 or 1 fp32 element).
-// K rows are contiguous in the pool, so a wave stores 256 contiguous bytes;
-// V is channel-major inside a block, so each element is its own 2/4-byte store.
+// One workgroup per (group of 8 new tokens, kv head).  K rows are contiguous in
+// the pool, so consecutive threads take consecutive channels of a token's row.
+// V is channel-major inside a block: a token's values are D elements bs apart.
+// For V the threads are laid out token-fastest -- thread (c, i) stores token
+// t0 + i of channels c, c + 32, ... -- so when the group's slots are
+// consecutive (a prefill chunk, at any alignment) eight neighbouring threads
+// write 8 neighbouring positions of one channel row, and their reads are 8
+// neighbouring channels of one token row.
+constexpr int kGroupTokens = 8;
+
 template <typename W>   // W = uint16_t (bf16) or uint32_t (fp32): the element's bits
 __global__ __launch_bounds__(256) void cache_write_kernel(
     W* __restrict__ kc, W* __restrict__ vc, const W* __restrict__ kn, const W* __restrict__ vn,
     const int64_t* __restrict__ slots, int32_t num_tokens, int32_t H, int32_t D, int32_t bs,
     int64_t num_slots) {
-    constexpr int E = 4 / sizeof(W);            // elements per 4-byte word
-    const int words = D / E;
-    const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    const int64_t total = static_cast<int64_t>(num_tokens) * H * words;
-    if (idx >= total) return;
-    const int wd = static_cast<int>(idx % words);
-    const int64_t th = idx / words;
-    const int g = static_cast<int>(th % H);
-    const int64_t t = th / H;
-    const int64_t slot = slots[t];
+    const int g = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kGroupTokens;
+    const int nt = static_cast<int>(min(static_cast<int64_t>(kGroupTokens), num_tokens - t0));
+
+    // K: token rows, channel-fastest
+    for (int e = tid; e < nt * D; e += 256) {
+        const int i = e / D, d = e % D;
+        const int64_t slot = slots[t0 + i];
+        if (slot < 0 || slot >= num_slots) continue;
+        const int64_t blk = slot / bs, off = slot % bs;
+        kc[((blk * H + g) * bs + off) * D + d] = kn[((t0 + i) * H + g) * D + d];
+    }
+    // V: token-fastest
+    const int i = tid % kGroupTokens;
+    if (i >= nt) return;
+    const int64_t slot = slots[t0 + i];
     if (slot < 0 || slot >= num_slots) return;
     const int64_t blk = slot / bs, off = slot % bs;
-    const int64_t src = (t * H + g) * D + static_cast<int64_t>(wd) * E;
-    const uint32_t word = *reinterpret_cast<const uint32_t*>(kn + src);
-    *reinterpret_cast<uint32_t*>(kc + ((blk * H + g) * bs + off) * D + static_cast<int64_t>(wd) * E) =
-        word;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const int64_t d = static_cast<int64_t>(wd) * E + e;
-        vc[((blk * H + g) * D + d) * bs + off] = vn[src + e];
-    }
+    const W* src = vn + ((t0 + i) * H + g) * D;
+    W* dst = vc + (blk * H + g) * D * static_cast<int64_t>(bs) + off;
+    for (int d = tid / kGroupTokens; d < D; d += 256 / kGroupTokens)
+        dst[static_cast<int64_t>(d) * bs] = src[d];
 }
 
 constexpr int kPairsPerLaunch = 128;
@@ -82,18 +91,16 @@ int pa_cache_write(void* k_cache, void* v_cache, const pa_cache_desc* desc, cons
     if (desc->head_dim % 2) return PA_ERR_UNSUPPORTED;
     const int32_t H = desc->num_kv_heads, D = desc->head_dim, bs = desc->block_size;
     const int64_t num_slots = static_cast<int64_t>(desc->num_blocks) * bs;
-    const int E = desc->kv_dtype == PA_BF16 ? 2 : 1;
-    const int64_t total = static_cast<int64_t>(num_tokens) * H * (D / E);
-    const int64_t grid = (total + 255) / 256;
-    if (grid > INT32_MAX) return PA_ERR_UNSUPPORTED;
+    const int64_t groups = (static_cast<int64_t>(num_tokens) + kGroupTokens - 1) / kGroupTokens;
+    if (groups > INT32_MAX || H > 65535) return PA_ERR_UNSUPPORTED;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const dim3 g(static_cast<uint32_t>(grid));
+    const dim3 grid(static_cast<uint32_t>(groups), static_cast<uint32_t>(H));
     if (desc->kv_dtype == PA_BF16)
-        return launch_kernel(cache_write_kernel<uint16_t>, g, dim3(256), 0, st,
+        return launch_kernel(cache_write_kernel<uint16_t>, grid, dim3(256), 0, st,
                              static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
                              static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
                              slot_mapping, num_tokens, H, D, bs, num_slots);
-    return launch_kernel(cache_write_kernel<uint32_t>, g, dim3(256), 0, st,
+    return launch_kernel(cache_write_kernel<uint32_t>, grid, dim3(256), 0, st,
                          static_cast<uint32_t*>(k_cache), static_cast<uint32_t*>(v_cache),
                          static_cast<const uint32_t*>(k_new), static_cast<const uint32_t*>(v_new),
                          slot_mapping, num_tokens, H, D, bs, num_slots);

@@ -69,15 +69,19 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kChunk = 32;                              // tokens per wave step
-constexpr int kWinChunks = 16;                          // chunks per window (512 tokens)
 constexpr int kMinBlock = 8;                            // smallest supported block size
-constexpr int kWinBlocks = kWinChunks * kChunk / kMinBlock + 1;   // block ids a window can touch
 constexpr int kMaxSeqsPerLaunch = 1024;                 // lengths scanned in LDS per launch
 constexpr int kMinPieceChunks = 4;                      // balanced: at least 128 tokens per range
-constexpr int kSeqsPerThread = kMaxSeqsPerLaunch / kThreads;
+constexpr int kMergeHeads = 8;                          // heads merged per LDS pass (12-wave groups)
+
+// Waves per SIMD the kernel is held to (register budget) and waves per
+// workgroup: fixed partitions use 4-wave workgroups, the balanced split one
+// workgroup that fills a CU (4 SIMDs x waves per SIMD).
+template <bool BF16, int D>
+constexpr int waves_per_simd() { return BF16 || D == 64 ? 3 : 2; }
+template <bool BF16, int D, bool FIXED>
+constexpr int waves_per_group() { return 4; }
 
 struct DecodeArgs {
     void* out;
@@ -128,8 +132,9 @@ __device__ __forceinline__ u32x4 ldg_nt(const char* p) {
 
 constexpr u32x4 kZero4 = {0u, 0u, 0u, 0u};
 
-// Exclusive prefix sum of one value per thread over the workgroup; *total
-// receives the sum.  Every thread must call it.
+// Exclusive prefix sum of one value per thread over a workgroup of NW waves;
+// *total receives the sum.  Every thread must call it.
+template <int NW>
 __device__ __forceinline__ int block_exscan(int v, int* s_tmp, int* total) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     int x = v;
@@ -142,7 +147,7 @@ __device__ __forceinline__ int block_exscan(int v, int* s_tmp, int* total) {
     __syncthreads();
     int before = 0, tot = 0;
 #pragma unroll
-    for (int i = 0; i < kWaves; ++i) {
+    for (int i = 0; i < NW; ++i) {
         const int t = s_tmp[i];
         before += i < w ? t : 0;
         tot += t;
@@ -176,9 +181,15 @@ struct ChunkRegs {
 
 // fp32 caches at head_dim 128 hold twice the registers per chunk and run at
 // two waves per SIMD; every other variant at three.
-template <bool BF16, int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 || D == 64 ? 3 : 2))) void decode_partition_kernel(
-    DecodeArgs a) {
+template <bool BF16, int D, bool FIXED>
+__global__ __launch_bounds__((64 * waves_per_group<BF16, D, FIXED>()))
+__attribute__((amdgpu_waves_per_eu((waves_per_simd<BF16, D>())))) void decode_partition_kernel(DecodeArgs a) {
+    constexpr int NW = waves_per_group<BF16, D, FIXED>();   // waves per workgroup
+    constexpr int NT = 64 * NW;
+    constexpr int WIN = 4 * NW;                              // chunks per window
+    constexpr int WINB = WIN * kChunk / kMinBlock + 1;       // block ids a window can touch
+    constexpr int SPT = (kMaxSeqsPerLaunch + NT - 1) / NT;   // lengths scanned per thread
+    constexpr int HG = FIXED ? 16 : kMergeHeads;             // heads per merge pass
     constexpr int ES = BF16 ? 2 : 4;
     using Regs = ChunkRegs<BF16, D>;
     constexpr int MT = D / 16;                    // output channel tiles
@@ -196,15 +207,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 |
     const float kNaN = __builtin_nanf("");
 
     // ---- LDS: (balanced split) lengths and their prefix sums; wave-merge buffers ----
-    const bool fixed = a.part_chunks > 0;
     extern __shared__ int s_dyn[];
     int* s_len = s_dyn;                           // [B]  L, or -1 for an invalid length
     int* s_cum = s_len + B;                       // [B+1] chunks per head before sequence s
-    float* s_acc = reinterpret_cast<float*>(fixed ? s_dyn : s_cum + B + 1);   // [4][G][D+4]
-    __shared__ int s_blk[2][kWinBlocks];
-    __shared__ float s_m[kWaves][16];
-    __shared__ float s_l[kWaves][16];
-    __shared__ int s_tmp[kWaves];
+    float* s_acc = reinterpret_cast<float*>(FIXED ? s_dyn : s_cum + B + 1);   // [NW][min(G, HG)][D+4]
+    __shared__ int s_blk[2][WINB];
+    __shared__ float s_m[NW][16];
+    __shared__ float s_l[NW][16];
+    __shared__ int s_tmp[NW];
 
     const int64_t tile_elems = static_cast<int64_t>(H) * bs * D;   // one block, all heads
     int buf = 0;                                                    // s_blk buffer in use
@@ -361,7 +371,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 |
             }
         };
 
-        // Windows of up to 16 chunks.  The window's block ids go to one of two
+        // Windows of up to 4 chunks per wave.  The window's block ids go to one of two
         // LDS buffers, so one barrier per window suffices: a buffer is written
         // again only two windows later, after every wave has passed the barrier
         // that follows its last use.  Block ids past the sequence's end are
@@ -369,8 +379,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 |
         // is never dereferenced.
 
         int bad = 0;
-        for (int wb = cb; wb < ce; wb += kWinChunks) {
-            const int we = min(ce, wb + kWinChunks);
+        for (int wb = cb; wb < ce; wb += WIN) {
+
+            const int we = min(ce, wb + WIN);
             const int fb = (wb * kChunk) / bs;
             const int nb = (we * kChunk - 1) / bs - fb + 1;
             int* ids = s_blk[buf];
@@ -387,10 +398,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 |
                 ids[tid] = id;
             }
             bad = __syncthreads_or(bad);
-            // Latency is hidden by occupancy (three workgroups per CU), not by
-            // a register double buffer: holding a second chunk needs ~280
+            // Latency is hidden by occupancy (three waves per SIMD), not by a
+            // register double buffer: holding a second chunk needs ~280
             // registers, which spills even at two waves per SIMD.
-            for (int ci = wb + w; ci < we; ci += kWaves) {
+            for (int ci = wb + w; ci < we; ci += NW) {
                 Regs R;
                 load_chunk(ci, fb, ids, R);
                 compute_chunk(ci, R);
@@ -398,7 +409,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 |
             buf ^= 1;
         }
 
-        // ---- merge the four waves through LDS ----
+        // ---- merge the waves through LDS, HG heads per pass ----
         const int rowstride = D + 4;
         float l_tot = l_run + __shfl_xor(l_run, 16);
         l_tot += __shfl_xor(l_tot, 32);
@@ -406,40 +417,44 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 |
             s_m[w][r] = m_run;
             s_l[w][r] = l_tot;
         }
-        if (r < G) {
-            float* dst = s_acc + (w * G + r) * rowstride;
+        const int hstride = min(G, HG);           // head rows per wave in s_acc
+        for (int h0 = 0; h0 < G; h0 += HG) {
+            const int hn = min(HG, G - h0);
+            if (h0 > 0) __syncthreads();          // the previous pass has read s_acc
+            if (r >= h0 && r < h0 + hn) {
+                float* dst = s_acc + (w * hstride + (r - h0)) * rowstride;
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+                for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) dst[mt * 16 + 4 * j + i] = acc[mt][i];
-        }
-        __syncthreads();
-
-        for (int e = tid; e < G * D; e += kThreads) {
-            const int h = e / D, d = e % D;
-            // a wave with no chunk in this partition has m = -inf and contributes 0
-            float M = s_m[0][h];
-#pragma unroll
-            for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, s_m[ww][h]);
-            float o = 0.f, l = 0.f;
-#pragma unroll
-            for (int ww = 0; ww < kWaves; ++ww) {
-                const float f = __builtin_amdgcn_exp2f(s_m[ww][h] - M);
-                o += f * s_acc[(ww * G + h) * rowstride + d];
-                l += f * s_l[ww][h];
+                    for (int i = 0; i < 4; ++i) dst[mt * 16 + 4 * j + i] = acc[mt][i];
             }
-            const int64_t sh = static_cast<int64_t>(s) * a.Hq + g * G + h;
-            if (npieces == 1) {
-                store_out(a.out, sh * D + d, bad ? kNaN : o / l, a.out_bf16);
-            } else {
-                a.ws_acc[(sh * a.pmax + piece) * D + d] = bad ? kNaN : o;
-                if (d == 0) a.ws_ml[sh * a.pmax + piece] = bad ? make_float2(kNaN, kNaN) : make_float2(M, l);
+            __syncthreads();
+            for (int e = tid; e < hn * D; e += NT) {
+                const int hl = e / D, d = e % D, h = h0 + hl;
+                // a wave with no chunk in this piece has m = -inf and contributes 0
+                float M = s_m[0][h];
+#pragma unroll
+                for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, s_m[ww][h]);
+                float o = 0.f, l = 0.f;
+#pragma unroll
+                for (int ww = 0; ww < NW; ++ww) {
+                    const float f = __builtin_amdgcn_exp2f(s_m[ww][h] - M);
+                    o += f * s_acc[(ww * hstride + hl) * rowstride + d];
+                    l += f * s_l[ww][h];
+                }
+                const int64_t sh = static_cast<int64_t>(s) * a.Hq + g * G + h;
+                if (npieces == 1) {
+                    store_out(a.out, sh * D + d, bad ? kNaN : o / l, a.out_bf16);
+                } else {
+                    a.ws_acc[(sh * a.pmax + piece) * D + d] = bad ? kNaN : o;
+                    if (d == 0) a.ws_ml[sh * a.pmax + piece] = bad ? make_float2(kNaN, kNaN) : make_float2(M, l);
+                }
+                if (piece == 0 && d == 0 && a.ws_np) a.ws_np[sh] = npieces;
             }
-            if (piece == 0 && d == 0 && a.ws_np) a.ws_np[sh] = npieces;
         }
     };
 
-    if (fixed) {
+    if constexpr (FIXED) {
         // One workgroup per (sequence, kv head, partition), dispatched by the
         // hardware as slots free up; partitions past a sequence's end exit at
         // once.  An invalid length gives NaN for the head group, written by
@@ -452,7 +467,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 |
         const int L = a.lens[s];
         if (L < 1 || L > a.max_ctx) {
             if (p == 0) {
-                for (int e = tid; e < G * D; e += kThreads)
+                for (int e = tid; e < G * D; e += NT)
                     store_out(a.out, (static_cast<int64_t>(s) * a.Hq + g * G) * D + e, kNaN, a.out_bf16);
                 if (a.ws_np && tid < G) a.ws_np[static_cast<int64_t>(s) * a.Hq + g * G + tid] = 0;
             }
@@ -467,11 +482,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 |
 
     // ---- balanced split: scan the lengths ----
     {
-        int cnt[kSeqsPerThread];
+        int cnt[SPT];
         int sum = 0;
 #pragma unroll
-        for (int i = 0; i < kSeqsPerThread; ++i) {
-            const int s = tid * kSeqsPerThread + i;
+        for (int i = 0; i < SPT; ++i) {
+            const int s = tid * SPT + i;
             int L = s < B ? a.lens[s] : -1;
             // the host guarantees max_ctx <= maxb * bs, so a valid L needs no
             // other bound to stay inside the block table
@@ -482,10 +497,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 |
             sum += cnt[i];
         }
         int tot;
-        int pre = block_exscan(sum, s_tmp, &tot);
+        int pre = block_exscan<NW>(sum, s_tmp, &tot);
 #pragma unroll
-        for (int i = 0; i < kSeqsPerThread; ++i) {
-            const int s = tid * kSeqsPerThread + i;
+        for (int i = 0; i < SPT; ++i) {
+            const int s = tid * SPT + i;
             if (s < B) s_cum[s] = pre;
             pre += cnt[i];
         }
@@ -496,10 +511,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 |
     // invalid lengths: NaN for every head and no piece (workgroup s % grid)
     for (int s = blockIdx.x; s < B; s += gridDim.x) {
         if (s_len[s] >= 0) continue;
-        for (int e = tid; e < a.Hq * D; e += kThreads)
+        for (int e = tid; e < a.Hq * D; e += NT)
             store_out(a.out, static_cast<int64_t>(s) * a.Hq * D + e, kNaN, a.out_bf16);
         if (a.ws_np)
-            for (int h = tid; h < a.Hq; h += kThreads) a.ws_np[static_cast<int64_t>(s) * a.Hq + h] = 0;
+            for (int h = tid; h < a.Hq; h += NT) a.ws_np[static_cast<int64_t>(s) * a.Hq + h] = 0;
     }
 
     // Ranges of Cw chunks over the (sequence, kv head, chunk) space, laid out
@@ -529,73 +544,81 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 |
     }
 }
 
-// One workgroup per (sequence, query head): merge the partitions of a head
-// that has more than one.  With M the largest partition max, each partition's
-// sum and output are weighted by 2^(m_p - M); the result is their ratio.
-// Thread t owns channel t % D and the partitions p = t / D (mod 256/D); the
-// partial sums are combined through LDS in a fixed order, so the result does
-// not depend on timing.
-__device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
+// Merge the pieces of every (sequence, query head) that has more than one: one
+// wave per (sequence, head), four per workgroup.  With M the largest piece max,
+// each piece's sum and output are weighted by 2^(m_p - M); the result is their
+// ratio.  Lane i owns channels i, i + 64 (D = 128) or i (D = 64); the pieces
+// are summed in a fixed order, so the result does not depend on timing.
+constexpr int kReduceWaves = 4;
+
+__device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const float o = __shfl_xor(v, off);
-        v = is_max ? fmaxf(v, o) : v + o;
-    }
-    const int w = threadIdx.x >> 6;
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) red[w] = v;
-    __syncthreads();
-    float r = red[0];
-#pragma unroll
-    for (int i = 1; i < 4; ++i) r = is_max ? fmaxf(r, red[i]) : r + red[i];
-    return r;
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    return v;
 }
 
-__global__ __launch_bounds__(256) void decode_reduce_kernel(void* out, int out_bf16,
-                                                           const float* __restrict__ ws_acc,
-                                                           const float2* __restrict__ ws_ml,
-                                                           const int32_t* __restrict__ ws_np, int32_t D,
-                                                           int32_t P) {
-    const int pair = blockIdx.x;
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * kReduceWaves) void decode_reduce_kernel(void* out, int out_bf16,
+                                                                         const float* __restrict__ ws_acc,
+                                                                         const float2* __restrict__ ws_ml,
+                                                                         const int32_t* __restrict__ ws_np,
+                                                                         int64_t pairs, int32_t P) {
+    constexpr int CPL = D / 64;                   // channels per lane
+    const int lane = threadIdx.x & 63;
+    const int64_t pair = static_cast<int64_t>(blockIdx.x) * kReduceWaves + (threadIdx.x >> 6);
+    if (pair >= pairs) return;
     const int np = min(ws_np[pair], P);
-    if (np <= 1) return;                                    // final already, or NaN written
-    __shared__ float red[4];
-    __shared__ float s_part[256];
-    const int tid = threadIdx.x;
-    const float2* ml = ws_ml + static_cast<int64_t>(pair) * P;
+    if (np <= 1) return;                          // final already, or NaN written
+    const float2* ml = ws_ml + pair * P;
     float m = -INFINITY;
-    for (int i = tid; i < np; i += 256) m = fmaxf(m, ml[i].x);
-    const float M = block_reduce(m, red, true);
+    for (int i = lane; i < np; i += 64) m = fmaxf(m, ml[i].x);
+    const float M = wave_max(m);
     float dp = 0.f;
-    for (int i = tid; i < np; i += 256) {
+    for (int i = lane; i < np; i += 64) {
         const float2 v = ml[i];
         dp += __builtin_amdgcn_exp2f(v.x - M) * v.y;
     }
-    const float den = block_reduce(dp, red, false);
-
-    const int groups = 256 / D;                             // D divides 256
-    const int d = tid % D, grp = tid / D;
-    const float* accp = ws_acc + static_cast<int64_t>(pair) * P * D + d;
-    // four independent partial sums keep four loads in flight per thread
-    float o[4] = {0.f, 0.f, 0.f, 0.f};
-    int i = grp;
-    for (; i + 3 * groups < np; i += 4 * groups) {
+    const float den = wave_sum(dp);
+    // Each lane computes the weight of one piece of a block of 64; the weights
+    // are broadcast with shuffles and the channel sums are kept in four
+    // independent accumulators, so four loads per lane are in flight.
+    const float* accp = ws_acc + pair * P * D + lane;
+    float o[4][CPL];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int pi = i + u * groups;
-            o[u] += __builtin_amdgcn_exp2f(ml[pi].x - M) * accp[static_cast<int64_t>(pi) * D];
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) o[u][c] = 0.f;
+    for (int b0 = 0; b0 < np; b0 += 64) {
+        const int nb = min(64, np - b0);
+        const float fl = lane < nb ? __builtin_amdgcn_exp2f(ml[b0 + lane].x - M) : 0.f;
+        int k = 0;
+        for (; k + 4 <= nb; k += 4) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float f = __shfl(fl, k + u);
+                const float* src = accp + static_cast<int64_t>(b0 + k + u) * D;
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) o[u][c] += f * src[64 * c];
+            }
+        }
+        for (; k < nb; ++k) {
+            const float f = __shfl(fl, k);
+            const float* src = accp + static_cast<int64_t>(b0 + k) * D;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) o[0][c] += f * src[64 * c];
         }
     }
-    for (int u = 0; i < np; i += groups, ++u)
-        o[u] += __builtin_amdgcn_exp2f(ml[i].x - M) * accp[static_cast<int64_t>(i) * D];
-    const float o0 = o[0] + o[2], o1 = o[1] + o[3];
-    s_part[tid] = o0 + o1;
-    __syncthreads();
-    if (grp == 0) {
-        float acc = s_part[d];
-        for (int g2 = 1; g2 < groups; ++g2) acc += s_part[g2 * D + d];
-        const float v = acc / den;
-        const int64_t idx = static_cast<int64_t>(pair) * D + d;
+    const float inv = 1.f / den;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const float v = ((o[0][c] + o[1][c]) + (o[2][c] + o[3][c])) * inv;
+        const int64_t idx = pair * D + lane + 64 * c;
         if (out_bf16)
             static_cast<__bf16*>(out)[idx] = static_cast<__bf16>(v);
         else
@@ -671,9 +694,10 @@ WsLayout workspace_layout(int64_t B, int64_t Hq, int64_t D, int64_t pmax, bool f
     return l;
 }
 
-size_t decode_lds_bytes(int32_t nseq, int32_t G, int32_t D, bool fixed) {
+size_t decode_lds_bytes(int32_t nseq, int32_t G, int32_t D, bool fixed, int waves) {
+    const int heads = fixed ? G : std::min(G, kMergeHeads);
     return (fixed ? 0 : static_cast<size_t>(2 * nseq + 1) * sizeof(int)) +
-           static_cast<size_t>(kWaves) * G * (D + 4) * sizeof(float);
+           static_cast<size_t>(waves) * heads * (D + 4) * sizeof(float);
 }
 
 // Compute units of the current device (cached per device).
@@ -700,7 +724,9 @@ int device_cus(int* cus) {
 
 template <bool BF16, int D>
 int launch_partitions(const DecodeArgs& a0, int32_t num_seqs, const Plan& c, hipStream_t st) {
-    const auto kernel = decode_partition_kernel<BF16, D>;
+    const bool fixed = c.part_chunks > 0;
+    const auto kernel = fixed ? decode_partition_kernel<BF16, D, true> : decode_partition_kernel<BF16, D, false>;
+    const int waves = fixed ? waves_per_group<BF16, D, true>() : waves_per_group<BF16, D, false>();
     int cus = 0;
     int rc = device_cus(&cus);
     if (rc != PA_OK) return rc;
@@ -720,8 +746,7 @@ int launch_partitions(const DecodeArgs& a0, int32_t num_seqs, const Plan& c, hip
             a.ws_ml = reinterpret_cast<float2*>(reinterpret_cast<char*>(a0.ws_ml) + s0 * per_seq_ml);
             a.ws_np = a0.ws_np + static_cast<int64_t>(s0) * a0.Hq;
         }
-        const bool fixed = c.part_chunks > 0;
-        const size_t lds = decode_lds_bytes(nb, c.G, D, fixed);
+        const size_t lds = decode_lds_bytes(nb, c.G, D, fixed, waves);
         int64_t grid;
         if (fixed) {
             // one workgroup per (sequence, kv head, partition slot)
@@ -731,14 +756,14 @@ int launch_partitions(const DecodeArgs& a0, int32_t num_seqs, const Plan& c, hip
             // as many workgroups as the chip holds at once, and no more than
             // minimal ranges of the longest context could keep busy
             int per_cu = 0;
-            rc = hip_status(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, lds));
+            rc = hip_status(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64 * waves, lds));
             if (rc != PA_OK) return rc;
             if (per_cu < 1) return PA_ERR_UNSUPPORTED;
             const int64_t nch = (static_cast<int64_t>(a.max_ctx) + kChunk - 1) / kChunk;
             const int64_t items = static_cast<int64_t>(nb) * a.H * ((nch + kMinPieceChunks - 1) / kMinPieceChunks);
             grid = std::max<int64_t>(1, std::min<int64_t>(static_cast<int64_t>(per_cu) * cus, items));
         }
-        rc = launch_kernel(kernel, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), lds, st, a);
+        rc = launch_kernel(kernel, dim3(static_cast<uint32_t>(grid)), dim3(64 * waves), lds, st, a);
         if (rc != PA_OK) return rc;
     }
     return PA_OK;
@@ -825,13 +850,15 @@ int pa_decode_reduce(void* out, int32_t out_dtype, const int32_t* context_lens, 
     if (ws.total == 0 || num_seqs == 0) return PA_OK;    // every head is a single partition
     if (!out || !workspace || workspace_bytes < ws.total) return PA_ERR_INVALID_ARG;
     const char* wsb = static_cast<const char*>(workspace);
-    const int64_t grid = static_cast<int64_t>(num_seqs) * num_q_heads;
+    const int64_t pairs = static_cast<int64_t>(num_seqs) * num_q_heads;
+    const int64_t grid = (pairs + kReduceWaves - 1) / kReduceWaves;
     if (grid > INT32_MAX) return PA_ERR_UNSUPPORTED;
-    return launch_kernel(decode_reduce_kernel, dim3(static_cast<uint32_t>(grid)), dim3(256), 0,
+    const auto kernel = head_dim == 128 ? decode_reduce_kernel<128> : decode_reduce_kernel<64>;
+    return launch_kernel(kernel, dim3(static_cast<uint32_t>(grid)), dim3(64 * kReduceWaves), 0,
                          static_cast<hipStream_t>(stream), out, out_dtype == PA_BF16,
                          reinterpret_cast<const float*>(wsb + ws.acc),
                          reinterpret_cast<const float2*>(wsb + ws.ml),
-                         reinterpret_cast<const int32_t*>(wsb + ws.np), head_dim, pmax);
+                         reinterpret_cast<const int32_t*>(wsb + ws.np), pairs, pmax);
 }
 
 int pa_decode(void* out, int32_t out_dtype, const void* q, const void* k_cache, const void* v_cache,
