@@ -145,6 +145,37 @@ int pa_seq_append_slots(pa_allocator* a, int32_t seq, int32_t n_tokens,
  * *n_cow_out = 1; otherwise nothing changes and *n_cow_out = 0. */
 int pa_seq_cow_block(pa_allocator* a, int32_t seq, int32_t logical_index,
                      int64_t* cow_pair_out, int32_t* n_cow_out);
+/* Automatic prefix caching ([studynote 528] section II key ideas and section
+ * IV: requests with the same system prompt share its blocks instead of
+ * recomputing them; [ch.09] closing section: finding reusable prompt blocks
+ * automatically).  Must be called before any block is allocated or sequence
+ * created (else PA_ERR_INVALID_ARG).  From then on:
+ *   - a full block's content is identified exactly by (the content of the
+ *     block before it, its block_size token ids);
+ *   - a block that fills with known content (through pa_seq_append_tokens) is
+ *     registered as the cached block of that content, unless one already is;
+ *   - a registered block whose count drops to zero keeps its contents on an
+ *     evictable list (oldest first) instead of returning to the free list;
+ *   - every allocation (pa_allocate_block, appends, copies) takes the free
+ *     list's head, else evicts the oldest evictable block. */
+int pa_allocator_enable_prefix_cache(pa_allocator* a);
+/* Number of evictable cached blocks (>= 0), or a negative status. */
+int32_t pa_num_cached(const pa_allocator* a);
+/* Grow `seq` by n_tokens tokens whose ids are token_ids[0..n_tokens-1].  As
+ * pa_seq_append_slots, except that with prefix caching on, each new block the
+ * call fills completely, in a sequence whose content is known, is looked up:
+ * if a block with the same content is cached, the sequence points at it (its
+ * count + 1) and slot_mapping_out holds -1 for its tokens -- their K/V is
+ * already in the pool, and pa_cache_write skips negative slots.
+ * *n_cached_out receives the number of such tokens.  Cache hits are taken
+ * before any fresh block of the call is allocated.  pa_seq_append_slots (no
+ * token ids) makes the sequence's content unknown: none of its later blocks
+ * is looked up or registered.  Without prefix caching this is
+ * pa_seq_append_slots with *n_cached_out = 0.  PA_ERR_OUT_OF_BLOCKS leaves
+ * everything unchanged. */
+int pa_seq_append_tokens(pa_allocator* a, int32_t seq, const int32_t* token_ids, int32_t n_tokens,
+                         int64_t* slot_mapping_out, int64_t* cow_pair_out, int32_t* n_cow_out,
+                         int32_t* n_cached_out);
 /* Release every block of `seq` (logical order) and forget the sequence. */
 int pa_seq_free(pa_allocator* a, int32_t seq);
 /* Tokens held by `seq` (>= 0), or a negative status. */

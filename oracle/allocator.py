@@ -88,6 +88,10 @@ class BlockAllocator:
     def num_free(self):
         return len(self.free)
 
+    def _available(self):
+        """Blocks an allocation can still obtain."""
+        return len(self.free)
+
     # -- sequences ---------------------------------------------------------------
     def _check_seq(self, seq):
         if seq not in self.tables:
@@ -132,7 +136,7 @@ class BlockAllocator:
         length = self.lengths[seq]
         needs_cow = (length % bs != 0) and self.refcount[table[-1]] > 1
         new_blocks = self._blocks_for(length + n) - self._blocks_for(length)
-        if new_blocks + (1 if needs_cow else 0) > len(self.free):
+        if new_blocks + (1 if needs_cow else 0) > self._available():
             raise OutOfBlocks("append needs more blocks than are free")
         cow = []
         if needs_cow:
@@ -163,6 +167,8 @@ class BlockAllocator:
         src = table[logical_index]
         if self.refcount[src] <= 1:
             return None
+        if self._available() == 0:
+            raise OutOfBlocks("no free block")
         dst = self.allocate_block()
         self.refcount[src] -= 1
         table[logical_index] = dst
@@ -190,6 +196,187 @@ class BlockAllocator:
         return tables, lens
 
 
+class PrefixCachingAllocator(BlockAllocator):
+    """The allocator with automatic prefix caching.
+
+    Written from: [studynote 528] section II, key ideas (requests with the same
+    system prompt share its blocks and skip re-computing it) and section IV
+    (prefix caching for a shared system prompt lowers the time to first
+    token); [ch.09] "09. PagedAttention", closing section (the next chapter's
+    subject: finding reusable prompt blocks automatically); [studynote 223]
+    section II copy-on-write paragraph (identical prefixes point at the same
+    physical blocks).  The pages give the idea, not the rules; the rules taken
+    here (each listed in the design doc):
+
+      * A full block's content is identified by (content of the block before
+        it, its block_size token ids); the first block's predecessor is the
+        empty prefix.  Identity is exact: equal ids mean equal token streams.
+      * append_tokens: a new block that the call fills completely, in a
+        sequence whose content is known so far, is looked up; if a block with
+        that content is cached, the sequence points at it (its count + 1) and
+        those tokens get slot -1 (their K/V is already in the pool).  Hits are
+        taken before any fresh block of the same call is allocated.
+      * A block that becomes full with known content is registered as the
+        cached block of that content, unless another block already is.
+      * When its count drops to zero, a registered block is kept, with its
+        contents, on an evictable list (oldest first) instead of the free
+        list.  An allocation takes the free list's head; if that is empty, it
+        evicts the oldest evictable block (which forgets its content).
+      * append_slots (no token ids) makes the sequence's content unknown: none
+        of its later blocks is looked up or registered.
+    """
+
+    ROOT = 0
+
+    def __init__(self, num_blocks, block_size, free_order=None):
+        super().__init__(num_blocks, block_size, free_order)
+        self.content_ids = {}                 # (parent content, tokens) -> content id (1, 2, ...)
+        self.cached = {}                      # content id -> physical block
+        self.content_of = [0] * num_blocks    # physical block -> content id it is registered under
+        self.evictable = []                   # registered blocks with count 0, oldest first
+        self.chain = {}                       # seq -> content id of its last full block, -1 unknown
+        self.pending = {}                     # seq -> token ids of its partial last block
+
+    def _available(self):
+        return len(self.free) + len(self.evictable)
+
+    def num_cached(self):
+        return len(self.evictable)
+
+    def allocate_block(self):
+        if self.free:
+            return super().allocate_block()
+        if not self.evictable:
+            raise OutOfBlocks("no free block")
+        b = self.evictable.pop(0)
+        del self.cached[self.content_of[b]]
+        self.content_of[b] = 0
+        self.refcount[b] = 1
+        return b
+
+    def free_block(self, block):
+        if not (0 <= block < self.num_blocks) or self.refcount[block] == 0:
+            raise BadBlock(f"block {block} is not allocated")
+        self.refcount[block] -= 1
+        if self.refcount[block] == 0:
+            (self.evictable if self.content_of[block] else self.free).append(block)
+
+    def create_seq(self):
+        s = super().create_seq()
+        self.chain[s] = self.ROOT
+        self.pending[s] = []
+        return s
+
+    def fork(self, parent):
+        child = super().fork(parent)
+        self.chain[child] = self.chain[parent]
+        self.pending[child] = list(self.pending[parent])
+        return child
+
+    def free_seq(self, seq):
+        super().free_seq(seq)
+        del self.chain[seq]
+        del self.pending[seq]
+
+    def append_slots(self, seq, n):
+        out = super().append_slots(seq, n)
+        if n:
+            self.chain[seq] = -1
+            self.pending[seq] = []
+        return out
+
+    def _content(self, parent, tokens, create):
+        key = (parent, tuple(int(t) for t in tokens))
+        cid = self.content_ids.get(key)
+        if cid is None and create:
+            cid = len(self.content_ids) + 1
+            self.content_ids[key] = cid
+        return cid
+
+    def append_tokens(self, seq, tokens):
+        """Grow `seq` by the given token ids.  Returns (slots, cow_pairs, n_cached):
+        slots as append_slots, with -1 for a token whose block was found in
+        the cache; n_cached counts those tokens."""
+        self._check_seq(seq)
+        tokens = [int(t) for t in tokens]
+        n = len(tokens)
+        if n == 0:
+            return [], [], 0
+        bs = self.block_size
+        table = self.tables[seq]
+        length = self.lengths[seq]
+        needs_cow = (length % bs != 0) and self.refcount[table[-1]] > 1
+        # plan: which new blocks are cache hits
+        chain = self.chain[seq]
+        pend = list(self.pending[seq])
+        hits = {}                             # logical block index -> cached physical block
+        new_blocks = 0
+        p = length
+        while p < length + n:
+            i = p - length
+            if p % bs == 0:
+                new_blocks += 1
+                full = p + bs <= length + n
+                if full and chain >= 0:
+                    cid = self._content(chain, tokens[i:i + bs], create=False)
+                    if cid is not None and cid in self.cached:
+                        hits[p // bs] = self.cached[cid]
+                    chain = self._content(chain, tokens[i:i + bs], create=True)
+                elif chain >= 0:
+                    pend = tokens[i:]         # a partial new block
+                p += bs if full else (length + n - p)
+            else:
+                # filling the existing partial block
+                take = min(bs - p % bs, length + n - p)
+                if chain >= 0:
+                    pend = pend + tokens[i:i + take]
+                    if len(pend) == bs:
+                        chain = self._content(chain, pend, create=True)
+                        pend = []
+                p += take
+        pinned = sum(1 for b in hits.values() if self.refcount[b] == 0)
+        if new_blocks - len(hits) + (1 if needs_cow else 0) > self._available() - pinned:
+            raise OutOfBlocks("append needs more blocks than are free")
+        # execute: hits first, then the copy-on-write block, then fresh blocks
+        for b in hits.values():
+            if self.refcount[b] == 0:
+                self.evictable.remove(b)
+            self.refcount[b] += 1
+        cow = []
+        if needs_cow:
+            src = table[-1]
+            dst = self.allocate_block()
+            self.refcount[src] -= 1
+            table[-1] = dst
+            cow.append((src, dst))
+        slots = []
+        n_cached = 0
+        chain = self.chain[seq]
+        pend = list(self.pending[seq])
+        for i, p in enumerate(range(length, length + n)):
+            lb = p // bs
+            if p % bs == 0:
+                table.append(hits[lb] if lb in hits else self.allocate_block())
+            if lb in hits:
+                slots.append(-1)
+                n_cached += 1
+            else:
+                slots.append(table[lb] * bs + p % bs)
+            if chain >= 0:
+                pend.append(tokens[i])
+                if len(pend) == bs:
+                    chain = self._content(chain, pend, create=True)
+                    pend = []
+                    b = table[lb]
+                    if chain not in self.cached:      # register (a hit is registered already)
+                        self.cached[chain] = b
+                        self.content_of[b] = chain
+        self.lengths[seq] = length + n
+        self.chain[seq] = chain
+        self.pending[seq] = pend if chain >= 0 else []
+        return slots, cow, n_cached
+
+
 def run_script(alloc, script):
     """Execute an op script (see workloads) and collect what each op returned.
 
@@ -211,6 +398,8 @@ def run_script(alloc, script):
         elif kind == "free":
             alloc.free_seq(op[1])
             results.append(None)
+        elif kind == "append_tokens":
+            results.append(alloc.append_tokens(op[1], op[2]))
         else:
             raise ValueError(f"unknown op {kind!r}")
     return results

@@ -105,6 +105,9 @@ _sig("pa_seq_fork", ctypes.c_int, _vp, _i32, _P32)
 _sig("pa_seq_append_slots", ctypes.c_int, _vp, _i32, _i32, _P64, _P64, _P32)
 _sig("pa_seq_cow_block", ctypes.c_int, _vp, _i32, _i32, _P64, _P32)
 _sig("pa_seq_free", ctypes.c_int, _vp, _i32)
+_sig("pa_allocator_enable_prefix_cache", ctypes.c_int, _vp)
+_sig("pa_num_cached", _i32, _vp)
+_sig("pa_seq_append_tokens", ctypes.c_int, _vp, _i32, _P32, _i32, _P64, _P64, _P32, _P32)
 _sig("pa_seq_length", _i32, _vp, _i32)
 _sig("pa_seq_block_table", ctypes.c_int, _vp, _i32, _P32, _i32, _P32)
 _sig("pa_build_block_tables", ctypes.c_int, _vp, _P32, _i32, _i32, _P32, _P32)
@@ -228,6 +231,32 @@ def pa_seq_cow_block(h, seq, logical_index):
     _check(_lib.pa_seq_cow_block(h, seq, logical_index, _i64p(pair), ctypes.byref(ncow)),
            "pa_seq_cow_block")
     return (int(pair[0]), int(pair[1])) if ncow.value else None
+
+
+def pa_allocator_enable_prefix_cache(h):
+    _check(_lib.pa_allocator_enable_prefix_cache(h), "pa_allocator_enable_prefix_cache")
+
+
+def pa_num_cached(h):
+    n = _lib.pa_num_cached(h)
+    if n < 0:
+        raise PAError(n, "pa_num_cached")
+    return n
+
+
+def pa_seq_append_tokens(h, seq, token_ids):
+    """Returns (slots int64 [n], cow_pairs list of (src, dst), n_cached)."""
+    toks = np.ascontiguousarray(token_ids, dtype=np.int32).reshape(-1)
+    n = len(toks)
+    slots = np.empty(max(n, 1), dtype=np.int64)
+    pair = np.empty(2, dtype=np.int64)
+    ncow = _i32()
+    ncached = _i32()
+    _check(_lib.pa_seq_append_tokens(h, seq, _i32p(toks) if n else None, n, _i64p(slots), _i64p(pair),
+                                     ctypes.byref(ncow), ctypes.byref(ncached)),
+           "pa_seq_append_tokens")
+    cow = [(int(pair[0]), int(pair[1]))] if ncow.value else []
+    return slots[:n], cow, ncached.value
 
 
 def pa_seq_free(h, seq):

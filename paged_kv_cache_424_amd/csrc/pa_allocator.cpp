@@ -15,10 +15,29 @@
 // so N slots suffice), seeded with the caller's order.  Reference counts per
 // block.  Sequences live in a vector indexed by id; ids are never reused.
 // Every call checks everything first and mutates only once it cannot fail.
+//
+// Automatic prefix caching (optional, [studynote 528] section II key ideas and
+// section IV: requests with the same system prompt share its blocks and skip
+// recomputing it; [ch.09] closing section: finding reusable prompt blocks is
+// the next step after paging).  A full block's content is identified exactly
+// by (the content id of the block before it, its block_size token ids); ids
+// are handed out 1, 2, ... and 0 is the empty prefix.  A block that fills with
+// known content is registered as the cached block of that content.  When its
+// reference count drops to zero, a registered block moves to an evictable
+// list (oldest first) with its contents intact instead of to the free list;
+// allocation takes a free block first and otherwise evicts the oldest
+// evictable one.  pa_seq_append_tokens looks each new full block up and, on a
+// hit, points the sequence at the cached block and reports slot -1 for its
+// tokens (their K/V is already in the pool).
 
+#include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <iterator>
+#include <list>
+#include <map>
 #include <new>
+#include <unordered_map>
 #include <vector>
 
 #include "../../include/pa.h"
@@ -29,6 +48,16 @@ struct Sequence {
     bool alive = false;
     int64_t length = 0;
     std::vector<int32_t> blocks;   // logical order
+    int64_t chain = 0;             // content id of the last full block; -1: content unknown
+    std::vector<int32_t> pending;  // token ids of the partial last block (content known)
+};
+
+struct ContentKey {
+    int64_t parent;
+    std::vector<int32_t> tokens;
+    bool operator<(const ContentKey& o) const {
+        return parent != o.parent ? parent < o.parent : tokens < o.tokens;
+    }
 };
 
 }  // namespace
@@ -41,6 +70,14 @@ struct pa_allocator {
     int32_t count = 0;             // number of free blocks
     std::vector<int32_t> refcount;
     std::vector<Sequence> seqs;
+    // prefix caching
+    bool caching = false;
+    std::map<ContentKey, int64_t> content_ids;
+    std::unordered_map<int64_t, int32_t> cached;   // content id -> registered block
+    std::vector<int64_t> content_of;               // block -> content id, 0 if not registered
+    std::list<int32_t> evictable;                  // registered blocks with count 0, oldest first
+    std::vector<std::list<int32_t>::iterator> evict_pos;
+    std::vector<char> in_evictable;
 
     int32_t pop_free() {
         int32_t b = ring[head];
@@ -53,8 +90,46 @@ struct pa_allocator {
         ring[(head + count) % num_blocks] = b;
         ++count;
     }
+    int64_t available() const { return count + static_cast<int64_t>(evictable.size()); }
+    // A block for a new owner: the free list's head, else the oldest evictable
+    // block, which forgets its content.  The caller has checked available().
+    int32_t take_block() {
+        if (count > 0) return pop_free();
+        const int32_t b = evictable.front();
+        evictable.pop_front();
+        in_evictable[b] = 0;
+        cached.erase(content_of[b]);
+        content_of[b] = 0;
+        refcount[b] = 1;
+        return b;
+    }
+    // One more owner of a cached block (taking it off the evictable list).
+    void take_cached(int32_t b) {
+        if (refcount[b] == 0 && in_evictable[b]) {
+            evictable.erase(evict_pos[b]);
+            in_evictable[b] = 0;
+        }
+        ++refcount[b];
+    }
     void drop_ref(int32_t b) {
-        if (--refcount[b] == 0) push_free(b);
+        if (--refcount[b] != 0) return;
+        if (content_of[b] != 0) {
+            evictable.push_back(b);
+            evict_pos[b] = std::prev(evictable.end());
+            in_evictable[b] = 1;
+        } else {
+            push_free(b);
+        }
+    }
+    // Content id of (parent, tokens); 0 when absent and create is false.
+    int64_t content(int64_t parent, const int32_t* tok, int32_t n, bool create) {
+        ContentKey k{parent, std::vector<int32_t>(tok, tok + n)};
+        auto it = content_ids.find(k);
+        if (it != content_ids.end()) return it->second;
+        if (!create) return 0;
+        const int64_t id = static_cast<int64_t>(content_ids.size()) + 1;
+        content_ids.emplace(std::move(k), id);
+        return id;
     }
     Sequence* seq(int32_t id) {
         if (id < 0 || id >= static_cast<int32_t>(seqs.size()) || !seqs[id].alive) return nullptr;
@@ -80,6 +155,9 @@ int pa_allocator_create(int32_t num_blocks, int32_t block_size,
         a->block_size = block_size;
         a->ring.resize(num_blocks);
         a->refcount.assign(num_blocks, 0);
+        a->content_of.assign(num_blocks, 0);
+        a->evict_pos.resize(num_blocks);
+        a->in_evictable.assign(num_blocks, 0);
         if (initial_free_order) {
             std::vector<char> seen(num_blocks, 0);
             for (int32_t i = 0; i < num_blocks; ++i) {
@@ -106,10 +184,21 @@ int pa_allocator_create(int32_t num_blocks, int32_t block_size,
 
 void pa_allocator_destroy(pa_allocator* a) { delete a; }
 
+int pa_allocator_enable_prefix_cache(pa_allocator* a) {
+    if (!a) return PA_ERR_INVALID_ARG;
+    if (!a->seqs.empty() || a->count != a->num_blocks) return PA_ERR_INVALID_ARG;
+    a->caching = true;
+    return PA_OK;
+}
+
+int32_t pa_num_cached(const pa_allocator* a) {
+    return a ? static_cast<int32_t>(a->evictable.size()) : PA_ERR_INVALID_ARG;
+}
+
 int pa_allocate_block(pa_allocator* a, int32_t* block_out) {
     if (!a || !block_out) return PA_ERR_INVALID_ARG;
-    if (a->count == 0) return PA_ERR_OUT_OF_BLOCKS;
-    *block_out = a->pop_free();
+    if (a->available() == 0) return PA_ERR_OUT_OF_BLOCKS;
+    *block_out = a->take_block();
     return PA_OK;
 }
 
@@ -149,6 +238,8 @@ int pa_seq_fork(pa_allocator* a, int32_t parent, int32_t* child_out) {
         child.alive = true;
         child.length = a->seqs[parent].length;
         child.blocks = a->seqs[parent].blocks;
+        child.chain = a->seqs[parent].chain;
+        child.pending = a->seqs[parent].pending;
         a->seqs.push_back(std::move(child));
     } catch (const std::bad_alloc&) {
         return PA_ERR_NO_MEMORY;
@@ -170,15 +261,19 @@ int pa_seq_append_slots(pa_allocator* a, int32_t seq, int32_t n_tokens,
     const int64_t len = s->length;
     const bool needs_cow = (len % bs != 0) && a->refcount[s->blocks.back()] > 1;
     const int64_t new_blocks = a->blocks_for(len + n_tokens) - a->blocks_for(len);
-    if (new_blocks + (needs_cow ? 1 : 0) > a->count) return PA_ERR_OUT_OF_BLOCKS;
+    if (new_blocks + (needs_cow ? 1 : 0) > a->available()) return PA_ERR_OUT_OF_BLOCKS;
     try {
         s->blocks.reserve(static_cast<size_t>(a->blocks_for(len + n_tokens)));
     } catch (const std::bad_alloc&) {
         return PA_ERR_NO_MEMORY;
     }
+    // tokens of unknown content: none of this sequence's later blocks can be
+    // looked up or registered
+    s->chain = -1;
+    s->pending.clear();
     if (needs_cow) {
         const int32_t src = s->blocks.back();
-        const int32_t dst = a->pop_free();
+        const int32_t dst = a->take_block();
         --a->refcount[src];                      // was > 1, stays >= 1
         s->blocks.back() = dst;
         cow_pair_out[0] = src;
@@ -187,10 +282,120 @@ int pa_seq_append_slots(pa_allocator* a, int32_t seq, int32_t n_tokens,
     }
     for (int64_t i = 0; i < n_tokens; ++i) {
         const int64_t p = len + i;
-        if (p % bs == 0) s->blocks.push_back(a->pop_free());
+        if (p % bs == 0) s->blocks.push_back(a->take_block());
         slot_mapping_out[i] = static_cast<int64_t>(s->blocks[p / bs]) * bs + p % bs;
     }
     s->length = len + n_tokens;
+    return PA_OK;
+}
+
+int pa_seq_append_tokens(pa_allocator* a, int32_t seq, const int32_t* token_ids, int32_t n_tokens,
+                         int64_t* slot_mapping_out, int64_t* cow_pair_out, int32_t* n_cow_out,
+                         int32_t* n_cached_out) {
+    if (!a || n_tokens < 0 || !n_cow_out || !cow_pair_out || !n_cached_out) return PA_ERR_INVALID_ARG;
+    if (n_tokens > 0 && (!slot_mapping_out || !token_ids)) return PA_ERR_INVALID_ARG;
+    *n_cached_out = 0;
+    if (!a->caching)
+        return pa_seq_append_slots(a, seq, n_tokens, slot_mapping_out, cow_pair_out, n_cow_out);
+    Sequence* s = a->seq(seq);
+    if (!s) return PA_ERR_BAD_SEQ;
+    *n_cow_out = 0;
+    if (n_tokens == 0) return PA_OK;
+    const int64_t bs = a->block_size;
+    const int64_t len = s->length;
+    const int64_t end = len + n_tokens;
+    const bool needs_cow = (len % bs != 0) && a->refcount[s->blocks.back()] > 1;
+    // ---- plan: which of the new blocks are found in the cache ----
+    std::vector<std::pair<int64_t, int32_t>> hits;   // (logical block, cached block)
+    int64_t new_blocks = 0, pinned = 0;
+    try {
+        s->blocks.reserve(static_cast<size_t>(a->blocks_for(end)));
+        s->pending.reserve(static_cast<size_t>(bs));
+        int64_t chain = s->chain;
+        std::vector<int32_t> pend = s->pending;
+        for (int64_t p = len; p < end;) {
+            const int64_t i = p - len;
+            if (p % bs == 0) {
+                ++new_blocks;
+                const bool full = p + bs <= end;
+                if (full && chain >= 0) {
+                    const int64_t cid = a->content(chain, token_ids + i, static_cast<int32_t>(bs), false);
+                    if (cid != 0) {
+                        auto it = a->cached.find(cid);
+                        if (it != a->cached.end()) {
+                            hits.emplace_back(p / bs, it->second);
+                            if (a->refcount[it->second] == 0) ++pinned;
+                        }
+                    }
+                    chain = a->content(chain, token_ids + i, static_cast<int32_t>(bs), true);
+                }
+                p += full ? bs : end - p;
+            } else {
+                const int64_t take = std::min<int64_t>(bs - p % bs, end - p);
+                if (chain >= 0) {
+                    pend.insert(pend.end(), token_ids + i, token_ids + i + take);
+                    if (static_cast<int64_t>(pend.size()) == bs) {
+                        chain = a->content(chain, pend.data(), static_cast<int32_t>(bs), true);
+                        pend.clear();
+                    }
+                }
+                p += take;
+            }
+        }
+    } catch (const std::bad_alloc&) {
+        return PA_ERR_NO_MEMORY;
+    }
+    const int64_t fresh = new_blocks - static_cast<int64_t>(hits.size()) + (needs_cow ? 1 : 0);
+    if (fresh > a->available() - pinned) return PA_ERR_OUT_OF_BLOCKS;
+    // ---- execute: hits first, then the copy-on-write block, then fresh blocks ----
+    for (const auto& h : hits) a->take_cached(h.second);
+    if (needs_cow) {
+        const int32_t src = s->blocks.back();
+        const int32_t dst = a->take_block();
+        --a->refcount[src];
+        s->blocks.back() = dst;
+        cow_pair_out[0] = src;
+        cow_pair_out[1] = dst;
+        *n_cow_out = 1;
+    }
+    size_t hi = 0;
+    int32_t n_cached = 0;
+    int64_t chain = s->chain;
+    std::vector<int32_t>& pend = s->pending;
+    // Every content id this loop needs was created by the plan and every
+    // vector is reserved; only registering a block can allocate (a map node).
+    try {
+    for (int64_t p = len; p < end; ++p) {
+        const int64_t lb = p / bs;
+        const bool hit = hi < hits.size() && hits[hi].first == lb;
+        if (p % bs == 0) s->blocks.push_back(hit ? hits[hi].second : a->take_block());
+        if (hit) {
+            slot_mapping_out[p - len] = -1;
+            ++n_cached;
+        } else {
+            slot_mapping_out[p - len] = static_cast<int64_t>(s->blocks[lb]) * bs + p % bs;
+        }
+        if (chain >= 0) {
+            pend.push_back(token_ids[p - len]);
+            if (static_cast<int64_t>(pend.size()) == bs) {
+                chain = a->content(chain, pend.data(), static_cast<int32_t>(bs), true);
+                pend.clear();
+                const int32_t b = s->blocks[lb];
+                if (a->cached.find(chain) == a->cached.end()) {   // register (a hit is already)
+                    a->cached.emplace(chain, b);
+                    a->content_of[b] = chain;
+                }
+            }
+        }
+        if (hit && (p + 1) % bs == 0) ++hi;
+    }
+    } catch (const std::bad_alloc&) {
+        return PA_ERR_NO_MEMORY;   // host memory exhausted while registering a block
+    }
+    s->length = end;
+    s->chain = chain;
+    if (chain < 0) pend.clear();
+    *n_cached_out = n_cached;
     return PA_OK;
 }
 
@@ -204,8 +409,8 @@ int pa_seq_cow_block(pa_allocator* a, int32_t seq, int32_t logical_index, int64_
     *n_cow_out = 0;
     const int32_t src = s->blocks[logical_index];
     if (a->refcount[src] <= 1) return PA_OK;
-    if (a->count == 0) return PA_ERR_OUT_OF_BLOCKS;
-    const int32_t dst = a->pop_free();
+    if (a->available() == 0) return PA_ERR_OUT_OF_BLOCKS;
+    const int32_t dst = a->take_block();
     --a->refcount[src];
     s->blocks[logical_index] = dst;
     cow_pair_out[0] = src;
@@ -222,6 +427,7 @@ int pa_seq_free(pa_allocator* a, int32_t seq) {
     s->alive = false;
     s->length = 0;
     std::vector<int32_t>().swap(s->blocks);
+    std::vector<int32_t>().swap(s->pending);
     return PA_OK;
 }
 

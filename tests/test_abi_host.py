@@ -256,3 +256,86 @@ def test_device_calls_reject_bad_host_arguments():
     # partition sizes must be multiples of 32 tokens
     assert pa.pa_decode_workspace_bytes(2, 8, 128, 1000, 100) == 0
     assert dec(one, 0, one, one, one, ref(desc), one, 4, one, 2, 8, 64, 0.1, 48, None, 0, None) == pa.PA_ERR_UNSUPPORTED
+
+
+# ---- prefix caching: C++ vs oracle ------------------------------------------------------------
+@pytest.mark.parametrize("seed", range(10))
+def test_prefix_cache_random_ops_bit_exact(seed):
+    from oracle.allocator import PrefixCachingAllocator
+    rnd = random.Random(2000 + seed)
+    N, bs = rnd.choice([(7, 2), (13, 4), (20, 3), (16, 8)])
+    order = rnd.sample(range(N), N)
+    o = PrefixCachingAllocator(N, bs, order)
+    h = pa.pa_allocator_create(N, bs, order)
+    pa.pa_allocator_enable_prefix_cache(h)
+    prompts = [[rnd.randint(0, 2) for _ in range(rnd.randint(1, 4 * bs))] for _ in range(5)]
+    try:
+        for step in range(600):
+            seqs = list(o.tables)
+            r = rnd.random()
+            if r < 0.2 or not seqs:
+                assert o.create_seq() == pa.pa_seq_create(h)
+                continue
+            s = rnd.choice(seqs)
+            if r < 0.28:
+                assert o.fork(s) == pa.pa_seq_fork(h, s)
+            elif r < 0.38:
+                o.free_seq(s)
+                pa.pa_seq_free(h, s)
+            elif r < 0.45:
+                n = rnd.randint(0, bs)
+                try:
+                    want = o.append_slots(s, n)
+                except OutOfBlocks:
+                    with pytest.raises(pa.PAError):
+                        pa.pa_seq_append_slots(h, s, n)
+                    continue
+                got = pa.pa_seq_append_slots(h, s, n)
+                assert (got[0].tolist(), got[1]) == (want[0], [tuple(p) for p in want[1]])
+            elif r < 0.5 and o.tables[s]:
+                i = rnd.randrange(len(o.tables[s]))
+                try:
+                    want = o.cow_block(s, i)
+                except OutOfBlocks:
+                    with pytest.raises(pa.PAError):
+                        pa.pa_seq_cow_block(h, s, i)
+                    continue
+                assert pa.pa_seq_cow_block(h, s, i) == want
+            else:
+                toks = (list(rnd.choice(prompts)) if o.lengths[s] == 0 else
+                        [rnd.randint(0, 2) for _ in range(rnd.randint(0, 2 * bs))])
+                try:
+                    want = o.append_tokens(s, toks)
+                except OutOfBlocks:
+                    with pytest.raises(pa.PAError) as e:
+                        pa.pa_seq_append_tokens(h, s, toks)
+                    assert e.value.status == pa.PA_ERR_OUT_OF_BLOCKS
+                    continue
+                got = pa.pa_seq_append_tokens(h, s, toks)
+                assert (got[0].tolist(), got[1], got[2]) == (want[0], [tuple(p) for p in want[1]], want[2])
+            seqs = list(o.tables)
+            assert [pa.pa_refcount(h, b) for b in range(N)] == o.refcount, step
+            assert {q: pa.pa_seq_block_table(h, q).tolist() for q in seqs} == {q: o.tables[q] for q in seqs}
+            assert pa.pa_num_free(h) == o.num_free() and pa.pa_num_cached(h) == o.num_cached()
+    finally:
+        pa.pa_allocator_destroy(h)
+
+
+def test_prefix_cache_must_be_enabled_on_a_fresh_allocator():
+    h = pa.pa_allocator_create(8, 4)
+    try:
+        pa.pa_seq_create(h)
+        with pytest.raises(pa.PAError):
+            pa.pa_allocator_enable_prefix_cache(h)
+    finally:
+        pa.pa_allocator_destroy(h)
+    h = pa.pa_allocator_create(8, 4)
+    try:
+        pa.pa_allocator_enable_prefix_cache(h)
+        s = pa.pa_seq_create(h)
+        slots, cow, n = pa.pa_seq_append_tokens(h, s, list(range(8)))
+        assert n == 0 and pa.pa_num_cached(h) == 0
+        pa.pa_seq_free(h, s)
+        assert pa.pa_num_cached(h) == 2 and pa.pa_num_free(h) == 6
+    finally:
+        pa.pa_allocator_destroy(h)
