@@ -33,9 +33,15 @@ class LibState:
 
 
 def run_script(w, alloc):
-    """Run the op script on the library allocator; return per-phase write lists."""
+    """Run the op script on the library allocator; return per-phase write lists.
+
+    Setup writes of a content-addressed workload are kept in script order,
+    one entry per op: a block freed and later evicted is written again by its
+    new owner, and the last write must win."""
     writes = {"setup": [], "step": []}     # (slots, rows)
     pairs = {"setup": [], "step": []}
+    if w.prefix_cache:
+        pa.pa_allocator_enable_prefix_cache(alloc)
     for phase, op in w.script:
         if op[0] == "create":
             pa.pa_seq_create(alloc)
@@ -51,6 +57,14 @@ def run_script(w, alloc):
             slots, cow = pa.pa_seq_append_slots(alloc, s, n)
             pairs[phase].extend(cow)
             writes[phase].append((slots, w.tok_rows[s][start:start + n]))
+        elif op[0] == "append_tokens":
+            s, toks = op[1], op[2]
+            start = pa.pa_seq_length(alloc, s)
+            slots, cow, _ = pa.pa_seq_append_tokens(alloc, s, toks)
+            pairs[phase].extend(cow)
+            writes[phase].append((slots, w.tok_rows[s][start:start + len(toks)]))
+        elif op[0] == "free":
+            pa.pa_seq_free(alloc, op[1])
         else:
             raise ValueError(op)
     return writes, pairs
@@ -83,7 +97,13 @@ def build(w, device="cuda", run_step=True):
     # (a prefix is written before it is shared, so copies of it see its data)
     if pairs["setup"]:
         raise NotImplementedError("copy-on-write during setup")
-    _write(st, w, writes["setup"], device)
+    st.setup_slots = (np.concatenate([sl for sl, _ in writes["setup"]]) if writes["setup"]
+                      else np.empty(0, dtype=np.int64))
+    if w.prefix_cache:
+        for item in writes["setup"]:
+            _write(st, w, [item], device)
+    else:
+        _write(st, w, writes["setup"], device)
     if run_step:
         if st.step_pairs:
             pa.pa_copy_blocks(st.kc, st.vc, st.desc, st.step_pairs)

@@ -8,7 +8,7 @@ workload's seeded inputs.
 import numpy as np
 
 from oracle import attention, cache
-from oracle.allocator import BlockAllocator
+from oracle.allocator import BlockAllocator, PrefixCachingAllocator
 
 
 class OracleState:
@@ -19,7 +19,7 @@ def build(w, run_step=True):
     """Run the workload's op script op by op: copy-on-write pairs are copied
     right away, then the append's tokens are written."""
     H, bs, D = w.num_kv_heads, w.block_size, w.head_dim
-    a = BlockAllocator(w.num_blocks, bs, w.free_order)
+    a = (PrefixCachingAllocator if w.prefix_cache else BlockAllocator)(w.num_blocks, bs, w.free_order)
     kpool = cache.new_pool(w.num_blocks, H, bs, D, w.dtype, w.fill_bits)
     vpool = cache.new_pool(w.num_blocks, H, bs, D, w.dtype, w.fill_bits)
     st = OracleState()
@@ -41,11 +41,12 @@ def build(w, run_step=True):
                 cache.copy_blocks(kpool, vpool, H, bs, D, w.num_blocks, [res])
                 if phase == "step":
                     st.step_pairs.append(res)
-        elif op[0] == "append":
-            s, n = op[1], op[2]
+        elif op[0] in ("append", "append_tokens"):
+            s = op[1]
+            n = op[2] if op[0] == "append" else len(op[2])
             start = a.lengths[s]
-            res = a.append_slots(s, n)
-            slots, cow = res
+            res = a.append_slots(s, n) if op[0] == "append" else a.append_tokens(s, op[2])
+            slots, cow = res[0], res[1]
             if cow:
                 cache.copy_blocks(kpool, vpool, H, bs, D, w.num_blocks, cow)
                 if phase == "step":
@@ -56,6 +57,8 @@ def build(w, run_step=True):
             if phase == "step":
                 st.step_slots.extend(slots)
                 st.step_rows.extend(rows.tolist())
+        elif op[0] == "free":
+            res = a.free_seq(op[1])
         else:
             raise ValueError(op)
         if phase == "setup":

@@ -339,3 +339,35 @@ def test_prefix_cache_must_be_enabled_on_a_fresh_allocator():
         assert pa.pa_num_cached(h) == 2 and pa.pa_num_free(h) == 6
     finally:
         pa.pa_allocator_destroy(h)
+
+
+@pytest.mark.parametrize("small", [True, False])
+def test_prompt_cache_workload_script_bit_exact(small):
+    # the shared-prompt workload's whole script (warm requests freed, batch
+    # hits their prompts, fresh blocks evict): every op's result is identical
+    from oracle.allocator import PrefixCachingAllocator
+    w = workloads.make("c4p", small=small)
+    o = PrefixCachingAllocator(w.num_blocks, w.block_size, w.free_order)
+    h = pa.pa_allocator_create(w.num_blocks, w.block_size, w.free_order)
+    pa.pa_allocator_enable_prefix_cache(h)
+    hits = 0
+    try:
+        for _, op in w.script:
+            if op[0] == "create":
+                assert o.create_seq() == pa.pa_seq_create(h)
+            elif op[0] == "free":
+                o.free_seq(op[1])
+                pa.pa_seq_free(h, op[1])
+            else:
+                want = o.append_tokens(op[1], op[2])
+                got = pa.pa_seq_append_tokens(h, op[1], op[2])
+                assert (got[0].tolist(), got[1], got[2]) == (want[0], [tuple(p) for p in want[1]], want[2])
+                hits += got[2]
+        tabs, lens = pa.pa_build_block_tables(h, w.decode_seqs, 128)
+        t_o, l_o = o.block_tables(w.decode_seqs, 128)
+        assert np.array_equal(tabs, np.asarray(t_o, dtype=np.int32))
+        assert np.array_equal(lens, np.asarray(l_o, dtype=np.int32))
+        assert pa.pa_num_free(h) == o.num_free() == 0      # the pool was tight: blocks were evicted
+        assert hits > 0
+    finally:
+        pa.pa_allocator_destroy(h)

@@ -23,7 +23,7 @@ pytestmark = pytest.mark.gpu
 TOL = {"f32": 1e-5, "bf16": 2e-2}
 BUDGET = {"f32": 2e-6, "bf16": 2e-4}
 
-SMALL = ["c1", "c2", "c3", "c4", "c4a", "c5"]
+SMALL = ["c1", "c2", "c3", "c4", "c4a", "c4p", "c5"]
 
 
 def _announce(msg):
@@ -142,6 +142,23 @@ def test_shared_prefix_bit_identical_to_duplicated(name):
     a = lib_run.decode(w, st)
     b = lib_run.decode(wd, lib_run.build(wd))
     assert torch.equal(a, b)
+
+
+def test_prompt_cache_bit_identical_to_duplicated():
+    # requests that found their prompt by content read the blocks another
+    # request wrote (some of them freed and evicted meanwhile): the same
+    # bits as every request holding private copies
+    w = workloads.make("c4p", small=True)
+    wd = workloads.relayout(w, duplicate_shared=True)
+    st = lib_run.build(w)
+    used = st.tables_host[st.tables_host >= 0]
+    assert len(np.unique(used)) < used.size           # some blocks are shared
+    assert np.any(st.setup_slots < 0)                 # some writes were skipped
+    std = lib_run.build(wd)
+    for part in (0, 32, 512):
+        a = lib_run.decode(w, st, partition_size=part)
+        b = lib_run.decode(wd, std, partition_size=part)
+        assert torch.equal(a, b), part
 
 
 # ---- probes with sharp structure -------------------------------------------------------

@@ -73,6 +73,7 @@ class Workload:
     chunk_len: list = field(default_factory=list)   # queries per chunk
     q_pre: np.ndarray = None    # [sum(chunk_len), Hq, D] stored values
     partition_size: int = 512
+    prefix_cache: bool = False  # the allocator finds reusable blocks by content
     note: str = ""
 
     @property
@@ -239,6 +240,85 @@ def c5_mixed(seed=5, n_decode=240, n_chunks=16, chunk=256, ctx_lo=256, ctx_hi=40
                     note=f"mixed step: {n_decode} decodes + {n_chunks}x{chunk} prefill queries")
 
 
+def c4_prompt_cache(seed=44, batch=32, n_prompts=4, prompt_lo=256, prompt_hi=1024, suffix_hi=512,
+                    n_warm=8, vocab=32000, bs=16, pool_margin=0.10):
+    """Shared system prompts found by content (automatic prefix caching), no forks.
+
+    Each of `batch` requests is one of `n_prompts` prompts (lengths
+    U{prompt_lo..prompt_hi}) followed by a private suffix of U{0..suffix_hi}
+    token ids and one decode token.  Before them, `n_warm` earlier requests of
+    the same form run and finish one after another, so the batch finds some
+    prompts only among freed blocks and its fresh blocks may evict them.
+
+    Token ids are U{0..vocab-1}, except that prompt i starts with id i, so two
+    prompts never coincide by chance.  A token's K/V depends on every token up
+    to it: rows of k_tok/v_tok are the nodes of the trie of all requests'
+    token lists (numbered in order of first appearance) and are drawn once per
+    node, so equal prefixes hold equal K/V.
+
+    Setup: each request is created and appends all its tokens but the last
+    through the content-addressed append; warm requests are then freed.  Step:
+    every batch request appends its decode token.  The pool holds the blocks
+    the batch needs when every prompt is shared, plus `pool_margin`: enough
+    for the batch, too few to keep every block the warm requests left, so
+    fresh blocks evict cached ones.
+    Draw order: prompt lengths and ids, request prompts and suffix lengths,
+    suffix ids, the free-block permutation, queries, keys, values.
+    """
+    rng = np.random.default_rng(seed)
+    Hq, Hkv, D = 32, 8, 128
+    plen = [int(x) for x in rng.integers(prompt_lo, prompt_hi + 1, size=n_prompts)]
+    prompts = []
+    for i, L in enumerate(plen):
+        ids = rng.integers(0, vocab, size=L)
+        ids[0] = i
+        prompts.append([int(x) for x in ids])
+    n_req = n_warm + batch
+    which = [int(x) for x in rng.integers(0, n_prompts, size=n_req)]
+    sfx = [int(x) for x in rng.integers(0, suffix_hi + 1, size=n_req)]
+    token_ids = {}
+    for r in range(n_req):
+        own = [int(x) for x in rng.integers(0, vocab, size=sfx[r] + 1)]
+        token_ids[r] = prompts[which[r]] + own
+    # trie of token lists -> K/V row per node
+    node = {}
+    tok_rows = {}
+    for r in range(n_req):
+        parent = -1
+        rows = []
+        for t in token_ids[r]:
+            key = (parent, t)
+            if key not in node:
+                node[key] = len(node)
+            parent = node[key]
+            rows.append(parent)
+        tok_rows[r] = np.asarray(rows, dtype=np.int64)
+    live = list(range(n_warm, n_req))
+    # blocks the batch holds: each prompt's full blocks once, the rest per request
+    # (equal suffixes could only lower this)
+    need = sum(plen[p] // bs for p in sorted({which[r] for r in live}))
+    need += sum(_ceil_div(len(token_ids[r]), bs) - plen[which[r]] // bs for r in live)
+    N = need + _ceil_div(int(need * pool_margin * 100), 100)
+    free_order = rng.permutation(N).astype(np.int32)
+    q = _normals(rng, (batch, Hq, D), "bf16")
+    k = _normals(rng, (len(node), Hkv, D), "bf16")
+    v = _normals(rng, (len(node), Hkv, D), "bf16")
+    script = []
+    for r in range(n_req):
+        script.append(("setup", ("create",)))
+        script.append(("setup", ("append_tokens", r, token_ids[r][:-1])))
+        if r < n_warm:
+            script.append(("setup", ("free", r)))
+    for r in live:
+        script.append(("step", ("append_tokens", r, token_ids[r][-1:])))
+    return Workload(name="c4p", dtype="bf16", num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                    block_size=bs, num_blocks=N, free_order=free_order,
+                    scale=1.0 / float(np.sqrt(D)), script=script, tok_rows=tok_rows,
+                    k_tok=k, v_tok=v, decode_seqs=live, q_dec=q, prefix_cache=True,
+                    note=f"{batch} requests over {n_prompts} prompts U{{{prompt_lo}..{prompt_hi}}} "
+                         f"found by content, suffix U{{0..{suffix_hi}}}, {n_warm} earlier requests freed")
+
+
 def make(name, small=False):
     """Full-size workload by name, or its scaled-down parity variant."""
     if name == "c1":
@@ -252,6 +332,9 @@ def make(name, small=False):
     if name == "c4a":
         return (c4_shared_prefix(batch=6, prefix=1024, suffix_hi=80, privatize_last_shared=True)
                 if small else c4_shared_prefix(prefix=1024, privatize_last_shared=True))
+    if name == "c4p":
+        return (c4_prompt_cache(batch=6, n_prompts=2, prompt_lo=20, prompt_hi=90, suffix_hi=40,
+                                n_warm=3) if small else c4_prompt_cache())
     if name == "c5":
         return (c5_mixed(n_decode=20, n_chunks=3, chunk=64, ctx_lo=64, ctx_hi=700, dec_hi=2000)
                 if small else c5_mixed())
