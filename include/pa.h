@@ -190,6 +190,34 @@ int pa_seq_block_table(const pa_allocator* a, int32_t seq, int32_t* table_out, i
 int pa_build_block_tables(const pa_allocator* a, const int32_t* seqs, int32_t n,
                           int32_t max_blocks, int32_t* tables_out, int32_t* context_lens_out);
 
+/* Occupancy of the pool, for capacity and fragmentation accounting.  The
+ * pages contrast the waste of reserving one contiguous region per request at
+ * its maximum length (internal fragmentation: slots reserved and never
+ * filled; external: free space cut into pieces too small to use) with paging,
+ * where waste is confined to the unfilled tail of each sequence's last block
+ * ([ch.09] "문제: 연속 할당의 단편화" and "해법: 페이지처럼 나눠 담기";
+ * [velog] "메모리 낭비 (Internal Fragmentation)").  Exact counts:
+ *   num_blocks     pool size;
+ *   free_blocks    blocks on the free list;
+ *   cached_blocks  count-0 blocks kept for prefix reuse (evictable);
+ *   used_blocks    blocks with count >= 1; shared_blocks: count >= 2;
+ *   live_seqs      sequences created and not freed;
+ *   logical_tokens sum of the live sequences' lengths;
+ *   stored_tokens  slots of used blocks that hold a token of some live
+ *                  sequence, each physical slot counted once however many
+ *                  sequences share it (slot o of block b is held when a
+ *                  sequence with b at logical index i has length > i*bs + o);
+ *   hit_tokens     tokens pa_seq_append_tokens found cached, since creation;
+ *   evictions      cached blocks handed to a new owner, since creation.
+ * So used_blocks*block_size - stored_tokens slots are allocated and empty,
+ * and sharing saves logical_tokens - stored_tokens slots.  Costs O(num_blocks
+ * + table entries); PA_ERR_NO_MEMORY if host scratch cannot be allocated. */
+typedef struct {
+    int32_t num_blocks, free_blocks, cached_blocks, used_blocks, shared_blocks, live_seqs;
+    int64_t logical_tokens, stored_tokens, hit_tokens, evictions;
+} pa_allocator_stats;
+int pa_allocator_get_stats(const pa_allocator* a, pa_allocator_stats* out);
+
 /* ---- device operations ------------------------------------------------------------ */
 
 /* Scatter new tokens into their cache slots ([studynote 223] section II figure:

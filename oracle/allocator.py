@@ -66,6 +66,8 @@ class BlockAllocator:
         self.tables = {}    # seq id -> list of physical block ids, logical order
         self.lengths = {}   # seq id -> number of tokens held
         self.next_seq = 0
+        self.hit_tokens = 0     # tokens found cached (prefix caching only)
+        self.evictions = 0      # cached blocks handed to a new owner (prefix caching only)
 
     # -- the pages' two calls ([velog] 메모리 할당자) ---------------------------
     def allocate_block(self):
@@ -91,6 +93,35 @@ class BlockAllocator:
     def _available(self):
         """Blocks an allocation can still obtain."""
         return len(self.free)
+
+    def num_cached(self):
+        return 0
+
+    def stats(self):
+        """Occupancy counts, for fragmentation accounting ([ch.09] "문제: 연속
+        할당의 단편화" and "해법: 페이지처럼 나눠 담기": with paging the only
+        waste is the unfilled tail of each sequence's last block).
+
+        stored_tokens is the number of distinct physical slots (block, offset)
+        that hold a position of some live sequence -- positions p < length
+        map to (table[p // bs], p mod bs) -- so a shared slot counts once."""
+        bs = self.block_size
+        held = set()
+        for s, table in self.tables.items():
+            for p in range(self.lengths[s]):
+                held.add((table[p // bs], p % bs))
+        return {
+            "num_blocks": self.num_blocks,
+            "free_blocks": len(self.free),
+            "cached_blocks": self.num_cached(),
+            "used_blocks": sum(1 for c in self.refcount if c >= 1),
+            "shared_blocks": sum(1 for c in self.refcount if c >= 2),
+            "live_seqs": len(self.tables),
+            "logical_tokens": sum(self.lengths.values()),
+            "stored_tokens": len(held),
+            "hit_tokens": self.hit_tokens,
+            "evictions": self.evictions,
+        }
 
     # -- sequences ---------------------------------------------------------------
     def _check_seq(self, seq):
@@ -249,6 +280,7 @@ class PrefixCachingAllocator(BlockAllocator):
         if not self.evictable:
             raise OutOfBlocks("no free block")
         b = self.evictable.pop(0)
+        self.evictions += 1
         del self.cached[self.content_of[b]]
         self.content_of[b] = 0
         self.refcount[b] = 1
@@ -374,6 +406,7 @@ class PrefixCachingAllocator(BlockAllocator):
         self.lengths[seq] = length + n
         self.chain[seq] = chain
         self.pending[seq] = pend if chain >= 0 else []
+        self.hit_tokens += n_cached
         return slots, cow, n_cached
 
 

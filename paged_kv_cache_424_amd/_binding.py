@@ -75,6 +75,13 @@ def cache_desc(num_blocks, block_size, num_kv_heads, head_dim, kv_dtype):
     return pa_cache_desc(num_blocks, block_size, num_kv_heads, head_dim, kv_dtype)
 
 
+class pa_allocator_stats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("num_blocks", "free_blocks", "cached_blocks",
+                                              "used_blocks", "shared_blocks", "live_seqs")] + \
+               [(n, ctypes.c_int64) for n in ("logical_tokens", "stored_tokens", "hit_tokens",
+                                              "evictions")]
+
+
 _i32, _i64, _f32, _sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
 _P32 = ctypes.POINTER(ctypes.c_int32)
 _P64 = ctypes.POINTER(ctypes.c_int64)
@@ -111,6 +118,7 @@ _sig("pa_seq_append_tokens", ctypes.c_int, _vp, _i32, _P32, _i32, _P64, _P64, _P
 _sig("pa_seq_length", _i32, _vp, _i32)
 _sig("pa_seq_block_table", ctypes.c_int, _vp, _i32, _P32, _i32, _P32)
 _sig("pa_build_block_tables", ctypes.c_int, _vp, _P32, _i32, _i32, _P32, _P32)
+_sig("pa_allocator_get_stats", ctypes.c_int, _vp, ctypes.POINTER(pa_allocator_stats))
 _sig("pa_cache_write", ctypes.c_int, _vp, _vp, _PD, _vp, _vp, _vp, _i32, _vp)
 _sig("pa_copy_blocks", ctypes.c_int, _vp, _vp, _PD, _P64, _i32, _vp)
 _sig("pa_decode_workspace_bytes", _sz, _i32, _i32, _i32, _i32, _i32)
@@ -257,6 +265,13 @@ def pa_seq_append_tokens(h, seq, token_ids):
            "pa_seq_append_tokens")
     cow = [(int(pair[0]), int(pair[1]))] if ncow.value else []
     return slots[:n], cow, ncached.value
+
+
+def pa_allocator_get_stats(h):
+    """Occupancy counts of the pool as a dict (fields of pa_allocator_stats)."""
+    st = pa_allocator_stats()
+    _check(_lib.pa_allocator_get_stats(h, ctypes.byref(st)), "pa_allocator_get_stats")
+    return {name: int(getattr(st, name)) for name, _ in pa_allocator_stats._fields_}
 
 
 def pa_seq_free(h, seq):

@@ -78,6 +78,9 @@ struct pa_allocator {
     std::list<int32_t> evictable;                  // registered blocks with count 0, oldest first
     std::vector<std::list<int32_t>::iterator> evict_pos;
     std::vector<char> in_evictable;
+    // cumulative counters for the occupancy statistics
+    int64_t hit_tokens = 0;
+    int64_t evictions = 0;
 
     int32_t pop_free() {
         int32_t b = ring[head];
@@ -98,6 +101,7 @@ struct pa_allocator {
         const int32_t b = evictable.front();
         evictable.pop_front();
         in_evictable[b] = 0;
+        ++evictions;
         cached.erase(content_of[b]);
         content_of[b] = 0;
         refcount[b] = 1;
@@ -395,6 +399,7 @@ int pa_seq_append_tokens(pa_allocator* a, int32_t seq, const int32_t* token_ids,
     s->length = end;
     s->chain = chain;
     if (chain < 0) pend.clear();
+    a->hit_tokens += n_cached;
     *n_cached_out = n_cached;
     return PA_OK;
 }
@@ -469,6 +474,41 @@ int pa_build_block_tables(const pa_allocator* a, const int32_t* seqs, int32_t n,
         for (int32_t j = 0; j < max_blocks; ++j) row[j] = j < nb ? s->blocks[j] : -1;
         context_lens_out[i] = static_cast<int32_t>(s->length);
     }
+    return PA_OK;
+}
+
+int pa_allocator_get_stats(const pa_allocator* a, pa_allocator_stats* out) {
+    if (!a || !out) return PA_ERR_INVALID_ARG;
+    pa_allocator_stats st{};
+    st.num_blocks = a->num_blocks;
+    st.free_blocks = a->count;
+    st.cached_blocks = static_cast<int32_t>(a->evictable.size());
+    for (int32_t b = 0; b < a->num_blocks; ++b) {
+        st.used_blocks += a->refcount[b] >= 1;
+        st.shared_blocks += a->refcount[b] >= 2;
+    }
+    // filled[b]: slots of block b below the longest reach of any holder
+    std::vector<int32_t> filled;
+    try {
+        filled.assign(a->num_blocks, 0);
+    } catch (const std::bad_alloc&) {
+        return PA_ERR_NO_MEMORY;
+    }
+    const int64_t bs = a->block_size;
+    for (const Sequence& s : a->seqs) {
+        if (!s.alive) continue;
+        ++st.live_seqs;
+        st.logical_tokens += s.length;
+        for (size_t i = 0; i < s.blocks.size(); ++i) {
+            const int64_t reach = std::min<int64_t>(bs, s.length - static_cast<int64_t>(i) * bs);
+            int32_t& f = filled[s.blocks[i]];
+            if (reach > f) f = static_cast<int32_t>(reach);
+        }
+    }
+    for (int32_t f : filled) st.stored_tokens += f;
+    st.hit_tokens = a->hit_tokens;
+    st.evictions = a->evictions;
+    *out = st;
     return PA_OK;
 }
 

@@ -146,6 +146,7 @@ def test_random_ops_bit_exact(seed):
             assert l.append_slots(s, n) == (want[0], [tuple(p) for p in want[1]])
         seqs = list(o.tables)
         assert oracle_state(o, seqs) == l.state(seqs)
+        assert pa.pa_allocator_get_stats(l.h) == o.stats()
 
 
 @pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c4a", "c5"])
@@ -317,6 +318,7 @@ def test_prefix_cache_random_ops_bit_exact(seed):
             assert [pa.pa_refcount(h, b) for b in range(N)] == o.refcount, step
             assert {q: pa.pa_seq_block_table(h, q).tolist() for q in seqs} == {q: o.tables[q] for q in seqs}
             assert pa.pa_num_free(h) == o.num_free() and pa.pa_num_cached(h) == o.num_cached()
+            assert pa.pa_allocator_get_stats(h) == o.stats()
     finally:
         pa.pa_allocator_destroy(h)
 
@@ -369,5 +371,8 @@ def test_prompt_cache_workload_script_bit_exact(small):
         assert np.array_equal(lens, np.asarray(l_o, dtype=np.int32))
         assert pa.pa_num_free(h) == o.num_free() == 0      # the pool was tight: blocks were evicted
         assert hits > 0
+        st = pa.pa_allocator_get_stats(h)
+        assert st == o.stats()
+        assert st["evictions"] > 0 and st["hit_tokens"] == hits
     finally:
         pa.pa_allocator_destroy(h)

@@ -122,6 +122,26 @@ def test_fragmentation_examples(golden):
     assert accounting.paged_waste(g["used"], g["block_size"]) == g["expected_empty"]
 
 
+def test_stats_worked_example():
+    # 10 tokens in 4-token blocks: 3 blocks, 2 empty slots in the last one
+    a = BlockAllocator(8, 4)
+    s = a.create_seq()
+    a.append_slots(s, 10)
+    st = a.stats()
+    assert (st["used_blocks"], st["free_blocks"], st["logical_tokens"], st["stored_tokens"]) == (3, 5, 10, 10)
+    assert 3 * 4 - st["stored_tokens"] == accounting.paged_waste(10, 4) == 2
+    # a fork shares all three blocks: twice the logical tokens, the same slots
+    c = a.fork(s)
+    st = a.stats()
+    assert (st["used_blocks"], st["shared_blocks"], st["logical_tokens"], st["stored_tokens"]) == (3, 3, 20, 10)
+    # the child's next token copies the partial block: positions 8..10 of the
+    # child in the copy, 8..9 of the parent in the original
+    a.append_slots(c, 1)
+    st = a.stats()
+    assert (st["used_blocks"], st["shared_blocks"], st["logical_tokens"], st["stored_tokens"]) == (4, 2, 21, 13)
+    assert (st["live_seqs"], st["hit_tokens"], st["evictions"], st["cached_blocks"]) == (2, 0, 0, 0)
+
+
 def test_errors_leave_state_unchanged():
     a = BlockAllocator(3, 4)
     s = a.create_seq()
@@ -156,6 +176,22 @@ def _check_invariants(a, live_len):
     assert len(set(free)) == len(free)
     assert set(free) == {b for b in range(N) if count[b] == 0}
     assert len(free) + sum(1 for c in count if c > 0) == N
+    # occupancy statistics, from the counts and the per-block reach of each holder
+    st = a.stats()
+    used = sum(1 for c in count if c > 0)
+    assert (st["free_blocks"], st["used_blocks"], st["shared_blocks"], st["live_seqs"]) == \
+        (len(free), used, sum(1 for c in count if c > 1), len(a.tables))
+    assert st["logical_tokens"] == sum(live_len.values())
+    reach = {}
+    for s, table in a.tables.items():
+        for i, b in enumerate(table):
+            reach[b] = max(reach.get(b, 0), min(bs, a.lengths[s] - i * bs))
+    assert st["stored_tokens"] == sum(reach.values())
+    assert st["stored_tokens"] <= min(st["logical_tokens"], used * bs)
+    if st["shared_blocks"] == 0:
+        assert st["stored_tokens"] == st["logical_tokens"]
+        assert used * bs - st["stored_tokens"] == sum(
+            accounting.paged_waste(L, bs) for L in a.lengths.values())
 
 
 @pytest.mark.parametrize("seed", range(12))

@@ -49,6 +49,8 @@ def test_freed_prompt_stays_cached_and_is_found_again():
     s2 = a.create_seq()
     _, _, n = a.append_tokens(s2, tokens((1, 9)))
     assert n == 8 and a.tables[s2] == full and a.num_cached() == 0
+    st = a.stats()
+    assert (st["hit_tokens"], st["evictions"], st["stored_tokens"], st["used_blocks"]) == (8, 0, 8, 2)
 
 
 def test_oldest_cached_block_is_evicted_first():
@@ -70,6 +72,8 @@ def test_oldest_cached_block_is_evicted_first():
     with pytest.raises(OutOfBlocks):
         a.append_tokens(s5, [9, 9, 8, 8])
     assert a.num_cached() == 0
+    st = a.stats()
+    assert (st["evictions"], st["hit_tokens"], st["used_blocks"], st["cached_blocks"]) == (4, 0, 4, 0)
 
 
 def test_partial_block_is_never_reused_and_first_difference_stops_reuse():
