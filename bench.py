@@ -11,7 +11,8 @@ resident in HBM:
 
 Prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--workload c2|c3|c4|c5]
+    python bench.py [--steps K] [--warmup W] [--workload c2|c3|c4|c4p|c5]
+    python bench.py --study prefix-cache|fragmentation|block-size|batch1
 
 Default workload (c2): Llama-3-8B-shaped decode.
 - 64 sequences, context lengths U{128..2048}.
@@ -55,6 +56,9 @@ WORKLOAD_TEXT = {
           "bf16 cache, 16-token blocks, 512-token partitions, keys x3",
     "c4": "shared-prefix decode with copy-on-write: 32 sequences share a 1016-token prefix "
           "(64 blocks), private suffix U{0..512} + 1 token, 32/8 heads, head_dim 128, bf16",
+    "c4p": "shared prompts found by content (automatic prefix caching): 32 requests over 4 prompts "
+           "of U{256..1024} tokens + private suffix U{0..512} + 1 token, 8 earlier requests freed, "
+           "tight pool (evictions), 32/8 heads, head_dim 128, bf16",
     "c5": "mixed continuous-batching step at 70B-shaped heads: 240 decodes (lognormal context, "
           "median 1024, [64, 8192]) + 16 prefill chunks of 256 queries over context U{256..4096}, "
           "64/8 heads, head_dim 128, bf16, 32-token blocks",
@@ -201,9 +205,15 @@ def main():
     ap.add_argument("--fetch-dir")
     ap.add_argument("--write-dir")
     ap.add_argument("--command", help="the profiled command, recorded in the summary")
+    ap.add_argument("--study", choices=["prefix-cache", "fragmentation", "block-size", "batch1"],
+                    help="run one of the studies in bench_studies.py instead of the benchmark")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(args)
+        return
+    if args.study:
+        import bench_studies
+        bench_studies.STUDIES[args.study](args)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -161,6 +161,38 @@ def test_prompt_cache_bit_identical_to_duplicated():
         assert torch.equal(a, b), part
 
 
+@pytest.mark.parametrize("bs", [8, 32, 64, 128])
+def test_block_sizes_match_oracle(bs):
+    # the Llama-3-8B-shaped batch stored with other block sizes (the sweep's
+    # configurations, at parity size)
+    _announce(f"decode c2 small, block size {bs}")
+    w = workloads.relayout(workloads.make("c2", small=True), block_size=bs, free_seed=77)
+    st_o, st_l = oracle_run.build(w), lib_run.build(w)
+    t_o, _ = oracle_run.decode_tables(w, st_o)
+    assert np.array_equal(np.asarray(t_o, dtype=np.int32), st_l.tables_host)
+    want = oracle_run.oracle_decode(w, st_o)
+    for part in (0, 512):
+        got = lib_run.decode(w, st_l, partition_size=part).double().cpu().numpy()
+        assert np.max(np.abs(got - want)) <= BUDGET["bf16"], part
+
+
+def test_single_sequence_scattered_and_in_order_blocks():
+    # one long sequence, blocks scattered over the pool or in order: the same
+    # bits, and the oracle's values (every head)
+    _announce("decode one sequence of 5000 tokens, two layouts")
+    w = workloads.decode_batch(seed=9, lens=[5000], name="b1")
+    wi = dataclasses.replace(w, free_order=np.arange(w.num_blocks, dtype=np.int32))
+    st_o = oracle_run.build(w)
+    want = oracle_run.oracle_decode(w, st_o)
+    st_s, st_i = lib_run.build(w), lib_run.build(wi)
+    assert not np.array_equal(st_s.tables_host, st_i.tables_host)
+    for part in (0, 512):
+        a = lib_run.decode(w, st_s, partition_size=part)
+        b = lib_run.decode(wi, st_i, partition_size=part)
+        assert torch.equal(a, b), part
+        assert np.max(np.abs(a.double().cpu().numpy() - want)) <= BUDGET["bf16"], part
+
+
 # ---- probes with sharp structure -------------------------------------------------------
 def _probe_workload(base, k=None, v=None, q=None):
     return dataclasses.replace(base, k_tok=base.k_tok if k is None else k,

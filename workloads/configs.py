@@ -137,6 +137,14 @@ def _decode_batch_from(rng, name, dtype, lens, Hq, Hkv, D, bs, k_mult=1.0, num_b
                     partition_size=partition_size, note=note)
 
 
+def decode_batch(seed, lens, name="decode", Hq=32, Hkv=8, D=128, bs=16, dtype="bf16"):
+    """A plain decode batch of the given context lengths (Llama-3-8B-shaped
+    heads by default), drawn as the decode workloads are."""
+    rng = np.random.default_rng(seed)
+    return _decode_batch_from(rng, name, dtype, list(lens), Hq, Hkv, D, bs,
+                              note=f"decode batch of {len(lens)} sequences")
+
+
 def c3_long(seed=3, batch=8, length=32768):
     """Long-context split-K decode: B 8 x 32768, 32/8 heads, D 128, bs 16, k x3."""
     rng = np.random.default_rng(seed)
