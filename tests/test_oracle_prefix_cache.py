@@ -7,14 +7,17 @@
     holds the K/V of (copy-on-write copies it too), and after every operation
     of random scripts each live sequence's block table must read back exactly
     its own history -- reuse may only ever map identical content;
-  * bookkeeping invariants recomputed from scratch after every operation.
+  * bookkeeping invariants recomputed from scratch after every operation;
+  * planted mistakes (a block identity that forgets its parent, an eviction
+    that keeps the old registration, a cached block sent to the free list)
+    that the content model must catch.
 """
 
 import random
 
 import pytest
 
-from oracle.allocator import OutOfBlocks, PrefixCachingAllocator
+from oracle.allocator import BlockAllocator, OutOfBlocks, PrefixCachingAllocator
 
 
 def tokens(*ranges):
@@ -212,3 +215,75 @@ def test_random_scripts_read_back_their_own_tokens(seed):
             pass
         m.check()
     assert hits > 0
+
+
+# ---- planted mistakes: the content model must catch each -----------------------------------
+class _KeyIgnoresParent(PrefixCachingAllocator):
+    """Bug: a block's identity forgets what came before it."""
+
+    def _content(self, parent, tokens, create):
+        return super()._content(0, tokens, create)
+
+
+class _EvictionKeepsMapping(PrefixCachingAllocator):
+    """Bug: an evicted block stays registered under its old content."""
+
+    def allocate_block(self):
+        if self.free:
+            return BlockAllocator.allocate_block(self)
+        if not self.evictable:
+            raise OutOfBlocks("no free block")
+        b = self.evictable.pop(0)
+        self.refcount[b] = 1
+        return b
+
+
+class _FreedGoesToFreeList(PrefixCachingAllocator):
+    """Bug: a cached block whose count drops to zero is freed but stays registered."""
+
+    def free_block(self, block):
+        self.refcount[block] -= 1
+        if self.refcount[block] == 0:
+            self.free.append(block)
+
+
+def _runs_clean(cls, seed):
+    rng = random.Random(seed)
+    bs = rng.choice([2, 3, 4])
+    n = rng.randint(6, 24)
+    a = cls(n, bs, free_order=rng.sample(range(n), n))
+    m = ContentModel(a)
+    prompts = [[rng.randint(0, 3) for _ in range(rng.randint(1, 12))] for _ in range(4)]
+    live = []
+    try:
+        for _ in range(400):
+            op = rng.random()
+            try:
+                if op < 0.3 or not live:
+                    s = a.create_seq()
+                    toks = list(rng.choice(prompts))
+                    slots, cow, _ = a.append_tokens(s, toks)
+                    m.after_append(s, toks, slots, cow)
+                    live.append(s)
+                elif op < 0.65:
+                    s = rng.choice(live)
+                    toks = [rng.randint(0, 3) for _ in range(rng.randint(1, 5))]
+                    slots, cow, _ = a.append_tokens(s, toks)
+                    m.after_append(s, toks, slots, cow)
+                else:
+                    s = rng.choice(live)
+                    a.free_seq(s)
+                    live.remove(s)
+                    del m.history[s]
+            except OutOfBlocks:
+                pass
+            m.check()
+    except (AssertionError, KeyError, ValueError):
+        return False
+    return True
+
+
+@pytest.mark.parametrize("mutant", [_KeyIgnoresParent, _EvictionKeepsMapping, _FreedGoesToFreeList])
+def test_planted_mistakes_are_caught(mutant):
+    assert all(_runs_clean(PrefixCachingAllocator, seed) for seed in range(6))
+    assert not all(_runs_clean(mutant, seed) for seed in range(6)), mutant.__doc__
