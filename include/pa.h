@@ -25,11 +25,14 @@
  *   - The calling thread's current HIP device is the one used.
  *
  * Cache layout (both pools are flat arrays of the cache dtype; H = kv heads,
- * bs = block_size, D = head_dim; slot s is token offset s % bs of block s / bs):
- *   K pool element (block b, head g, offset o, channel d) at ((b*H + g)*bs + o)*D + d
+ * bs = block_size, D = head_dim, W = 32 channels per K group when D is a
+ * multiple of 32, else W = D; slot s is token offset s % bs of block s / bs):
+ *   K pool element (block b, head g, offset o, channel d) at
+ *       (b*H + g)*bs*D + ((d / W)*bs + o)*W + d % W
  *   V pool element (block b, head g, offset o, channel d) at ((b*H + g)*D + d)*bs + o
- * so one (block, head) tile is contiguous in each pool: K as bs token rows of
- * D channels, V as D channel rows of bs tokens.  pa_kv_offset() evaluates this.
+ * so one (block, head) tile is contiguous in each pool: K as D/W groups of bs
+ * token rows of W channels, V as D channel rows of bs tokens.  pa_kv_offset()
+ * evaluates this.
  */
 #ifndef PA_H
 #define PA_H

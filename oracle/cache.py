@@ -9,7 +9,10 @@ block are arranged.  The arrangement is a design choice of the library; this
 module writes that choice out independently, from its statement:
 
   K pool, element (block b, kv head g, token offset o, channel d) lives at
-      ((b * H + g) * bs + o) * D + d          (one token row of D channels)
+      (b * H + g) * bs * D + ((d // W) * bs + o) * W + d % W
+                                 (groups of W channels, W = 32 when D is a
+                                  multiple of 32, else W = D; within a group,
+                                  one token row of W channels)
   V pool, the same element lives at
       ((b * H + g) * D + d) * bs + o          (one channel row of bs tokens)
 
@@ -27,7 +30,8 @@ import numpy as np
 
 
 def k_index(H, bs, D, block, head, offset, dim):
-    return ((block * H + head) * bs + offset) * D + dim
+    W = 32 if D % 32 == 0 else D
+    return (block * H + head) * bs * D + ((dim // W) * bs + offset) * W + dim % W
 
 
 def v_index(H, bs, D, block, head, offset, dim):

@@ -15,8 +15,10 @@
 namespace pa {
 namespace {
 
-// One workgroup per (group of 8 new tokens, kv head).  K rows are contiguous in
-// the pool, so consecutive threads take consecutive channels of a token's row.
+// One workgroup per (group of 8 new tokens, kv head).  Inside a block, K is
+// stored as groups of W channels (32, or D when D is not a multiple of 32), each a run of bs token rows of W
+// channels; consecutive threads take consecutive channels of one group, token
+// after token, so the writes of consecutive slots are consecutive addresses.
 // V is channel-major inside a block: a token's values are D elements bs apart.
 // For V the threads are laid out token-fastest -- thread (c, i) stores token
 // t0 + i of channels c, c + 32, ... -- so when the group's slots are
@@ -35,13 +37,16 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
     const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kGroupTokens;
     const int nt = static_cast<int>(min(static_cast<int64_t>(kGroupTokens), num_tokens - t0));
 
-    // K: token rows, channel-fastest
+    // K: channel group slowest, then token, then channel within the group
+    const int GW = D % 32 == 0 ? 32 : D;          // channels per K group
     for (int e = tid; e < nt * D; e += 256) {
-        const int i = e / D, d = e % D;
+        const int grp = e / (nt * GW), i = (e / GW) % nt, dl = e % GW;
+        const int d = grp * GW + dl;
         const int64_t slot = slots[t0 + i];
         if (slot < 0 || slot >= num_slots) continue;
         const int64_t blk = slot / bs, off = slot % bs;
-        kc[((blk * H + g) * bs + off) * D + d] = kn[((t0 + i) * H + g) * D + d];
+        kc[(blk * H + g) * bs * D + (grp * static_cast<int64_t>(bs) + off) * GW + dl] =
+            kn[((t0 + i) * H + g) * D + d];
     }
     // V: token-fastest
     const int i = tid % kGroupTokens;

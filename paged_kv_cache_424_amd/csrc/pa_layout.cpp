@@ -42,7 +42,10 @@ int64_t pa_kv_offset(const pa_cache_desc* d, int32_t which, int64_t slot, int32_
         dim < 0 || dim >= D)
         return -1;
     const int64_t block = slot / bs, off = slot % bs;
-    if (which == 0) return ((block * H + head) * bs + off) * D + dim;   // token rows
+    if (which == 0) {                                                   // groups of token rows
+        const int64_t W = D % 32 == 0 ? 32 : D;
+        return (block * H + head) * bs * D + ((dim / W) * bs + off) * W + dim % W;
+    }
     return ((block * H + head) * D + dim) * bs + off;                   // channel rows
 }
 

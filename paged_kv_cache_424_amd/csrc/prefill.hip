@@ -192,21 +192,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int nblk = (Lc + bs - 1) / bs;
     const int32_t* trow = a.tables + static_cast<int64_t>(c) * a.maxb;
     int bad = 0;
+    // The table entry of block i of tile t (0 past the context: any valid
+    // block, masked later), and its check: an id outside the pool marks the
+    // workgroup bad and is replaced by block 0, so it is never dereferenced.
+    auto block_index = [&](int t, int i) { return (t * kKT) / bs + i; };
+    auto raw_block_id = [&](int b) { return trow[min(b, nblk - 1)]; };   // nblk >= 1
+    auto checked = [&](int b, int id) -> int {    // branch-free
+        const bool inside = b < nblk;
+        const bool ok = id >= 0 && id < a.N;
+        bad |= (inside && !ok) ? 1 : 0;
+        return inside && ok ? id : 0;
+    };
     auto block_id = [&](int t, int i) -> int {
-        const int b = (t * kKT) / bs + i;
-        if (b >= nblk) return 0;                 // past the context: any valid block, masked later
-        const int id = trow[b];
-        if (id < 0 || id >= a.N) {
-            bad = 1;
-            return 0;
-        }
-        return id;
+        const int b = block_index(t, i);
+        return checked(b, raw_block_id(b));
     };
 
     // ---- tile loader: each thread moves 4 K segments and 4 V segments of 16 bytes ----
     // K segment p: key (tid / 16) + 16 p of the tile, channels 8 (tid % 16) ..
-    // +7.  V segment p: channel (tid / 8) + 32 p, keys 8 (tid % 8) .. +7 (one
-    // block, as block_size >= 8).  With block_size <= 64 a tile starts on a
+    // +7, which sit in 32-channel group (tid % 16) / 4 of the block: the four
+    // keys of a quarter-wave are adjacent 64-byte rows of that group.  V
+    // segment p: channel (tid / 8) + 32 p, keys 8 (tid % 8) .. +7 (one block,
+    // as block_size >= 8).  With block_size <= 64 a tile starts on a
     // block boundary, so a segment's block slot and in-block offset are the
     // same for every tile and are computed once here; larger blocks add the
     // tile's offset inside its block.
@@ -220,7 +227,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int p = 0; p < 4; ++p) {
         const int key = (tid >> 4) + 16 * p;
         kslot[p] = big_blocks ? 0 : key >> log2bs;
-        koff[p] = ((big_blocks ? key : key & (bs - 1)) * kD + (tid & 15) * 8) * 2;   // bytes
+        const int grp = (tid & 15) >> 2;                       // 32-channel group
+        koff[p] = ((grp * bs + (big_blocks ? key : key & (bs - 1))) * 32 + (tid & 3) * 8) * 2;   // bytes
     }
     const int vkey = 8 * (tid & 7);
     const int vslot = big_blocks ? 0 : vkey >> log2bs;
@@ -233,7 +241,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int in_blk = big_blocks ? (base & (bs - 1)) : 0;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            const char* src = kbase + ids[kslot[p]] * tile_bytes + koff[p] + in_blk * kD * 2;
+            const char* src = kbase + ids[kslot[p]] * tile_bytes + koff[p] + in_blk * 32 * 2;
             pk[p] = *reinterpret_cast<const u32x4*>(src);
         }
         const char* vsrc = vbase + ids[vslot] * tile_bytes + voff + in_blk * 2;
@@ -284,8 +292,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int buf = kt & 1;
         const int base = kt * kKT;
         if (kt + 1 < nkt) load_tile(kt + 1, s_ids[buf ^ 1]);
-        int nid = 0;
-        if (kt + 2 < nkt && tid < n_ids) nid = block_id(kt + 2, tid);
+        // tile kt + 2's block ids: loaded now, checked and stored after this
+        // tile's math, so the wait for them is not on the critical path
+        // Every thread loads and checks one id in every iteration (lanes
+        // past n_ids, and iterations with no tile kt + 2, repeat an id
+        // already read), so the load is always consumed on the same path.
+        const bool next_ids = kt + 2 < nkt;
+        const int nb_idx = block_index(min(kt + 2, nkt - 1), min(tid, n_ids - 1));
+        const int nid = raw_block_id(nb_idx);
 
         // ---- logits S^T[key][row] for the tile's two 32-key MFMA tiles ----
         f32x16_t st[2];
@@ -353,7 +367,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             }
         }
         if (kt + 1 < nkt) store_tile(buf ^ 1);
-        if (kt + 2 < nkt && tid < n_ids) s_ids[buf][tid] = nid;
+        const int id = checked(nb_idx, nid);
+        if (next_ids && tid < n_ids) s_ids[buf][tid] = id;
         __syncthreads();
     }
     bad = __syncthreads_or(bad);
