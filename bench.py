@@ -18,7 +18,8 @@ Default workload (c2): Llama-3-8B-shaped decode.
 - 64 sequences, context lengths U{128..2048}.
 - 32 query / 8 KV heads, head_dim 128.
 - bf16 cache in 16-token blocks, pool = blocks needed + 10 %.
-- One new token per sequence is written, then decoded.
+- One new token per sequence is written, then decoded in 512-token
+  partitions (--partition; 0 selects the balanced split).
 
 Consecutive steps read different copies of the pools, at least 1 GiB apart
 in total, so no step is served from the 256 MB Infinity Cache that the
@@ -191,9 +192,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c2", choices=sorted(WORKLOAD_TEXT))
-    ap.add_argument("--partition", type=int, default=None,
+    ap.add_argument("--partition", type=int, default=512,
                     help="split-K partition in tokens (a multiple of 32), or 0 for the balanced split; "
-                         "default: 512 for the long-context workload (its stated partition), else 0")
+                         "default 512, the method's stated partition size")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the extra HIP-graph replay measurement of the whole step")
@@ -227,8 +228,6 @@ def main():
     import workloads
     from tests import lib_run
 
-    if args.partition is None:
-        args.partition = 512 if args.workload == "c3" else 0
     torch.cuda.set_device(0)
     print(f"[bench] workload {args.workload}: generating inputs", file=sys.stderr, flush=True)
     w = workloads.make(args.workload)

@@ -26,8 +26,9 @@ fragmentation: a saturated request queue served with continuous batching
     figures (60-80 % waste, under 4 %) come from traces that are not here:
     the synthetic length mix below is stated, not theirs.
 block-size: the Llama-3-8B-shaped decode batch stored with 8, 16, 32, 64 and
-    128-token blocks: partition-kernel time and GB/s against the slots left
-    empty in last blocks and the size of the block tables.  [studynote 223]
+    128-token blocks (512-token partitions): partition-kernel time and GB/s
+    against the slots left empty in last blocks and the size of the block
+    tables.  [studynote 223]
     section IV, checklist item 1; [ch.09] "한계와 트레이드오프".
 batch1: one sequence of 512..32768 tokens, its blocks scattered over the pool
     or laid out in order (identity table), beside 64 sequences of the same
@@ -360,7 +361,7 @@ def study_block_size(args):
         st = lib_run.build(w)
         lens = st.lens_host.astype(np.int64)
         stats = pa.pa_allocator_get_stats(st.alloc)
-        part_us, red_us, copies = _time_decode(w, st, 0, args.steps)
+        part_us, red_us, copies = _time_decode(w, st, 512, args.steps)
         algo = _algo_bytes(w, lens)
         _emit({"study": "block_size", "workload": "c2 decode batch: 64 sequences, context U{128..2048}, "
                                                   "32/8 heads, head_dim 128, bf16",
