@@ -193,6 +193,27 @@ def test_single_sequence_scattered_and_in_order_blocks():
         assert np.max(np.abs(a.double().cpu().numpy() - want)) <= BUDGET["bf16"], part
 
 
+@pytest.mark.parametrize("dtype,D,G,bs", [
+    ("bf16", 128, 1, 16), ("bf16", 128, 2, 8), ("bf16", 128, 3, 32), ("bf16", 128, 16, 16),
+    ("bf16", 64, 4, 16), ("bf16", 64, 8, 64), ("bf16", 64, 5, 8), ("bf16", 128, 12, 128),
+    ("f32", 128, 4, 16), ("f32", 64, 2, 32), ("f32", 128, 16, 8), ("f32", 64, 7, 16)])
+def test_decode_shapes(dtype, D, G, bs):
+    # head groups from 1 to 16 (powers of two or not), both head sizes, both
+    # cache dtypes, block sizes 8..128; lengths include 1, exact multiples of
+    # a block and of a 32-token chunk, and a ragged tail
+    _announce(f"decode shapes {dtype} D={D} G={G} bs={bs}")
+    rng = np.random.default_rng(D + 7 * G + bs)
+    lens = [1, bs, 32, 96, 511, 512, 513] + [int(x) for x in rng.integers(2, 1500, size=3)]
+    w = workloads.decode_batch(seed=D * 100 + G, lens=lens, name="shapes", Hq=2 * G, Hkv=2, D=D,
+                               bs=bs, dtype=dtype)
+    st_o, st_l = oracle_run.build(w), lib_run.build(w)
+    want = oracle_run.oracle_decode(w, st_o)
+    for part in (0, 32, 512):
+        got = lib_run.decode(w, st_l, partition_size=part).double().cpu().numpy()
+        assert np.isfinite(got).all(), part
+        assert np.max(np.abs(got - want)) <= BUDGET[dtype], part
+
+
 # ---- probes with sharp structure -------------------------------------------------------
 def _probe_workload(base, k=None, v=None, q=None):
     return dataclasses.replace(base, k_tok=base.k_tok if k is None else k,
