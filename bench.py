@@ -5,7 +5,9 @@ A step is one pass of the hot path over one batch, with every input already
 resident in HBM:
 
 1. the copy-on-write block copies, when the workload has shared prefixes;
-2. the cache write of every token the step appends;
+2. the cache write of the tokens the step appends; when those are only each
+   decode sequence's newest token, the decode kernel stores them itself
+   instead (pa_decode_append; --append on/off overrides);
 3. the split-K decode partition kernel, then the rescaling reduce;
 4. for the mixed continuous-batching workload, the prefill-chunk kernel.
 
@@ -195,6 +197,10 @@ def main():
     ap.add_argument("--partition", type=int, default=512,
                     help="split-K partition in tokens (a multiple of 32), or 0 for the balanced split; "
                          "default 512, the method's stated partition size")
+    ap.add_argument("--append", choices=["auto", "on", "off"], default="auto",
+                    help="store each decode sequence's newest token inside the decode kernel "
+                         "(pa_decode_append) instead of a separate cache write; auto: when the "
+                         "step writes no other token (a cache-write launch happens anyway otherwise)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the extra HIP-graph replay measurement of the whole step")
@@ -240,9 +246,26 @@ def main():
     # the step's inputs: the tokens the step appends (the new token of every
     # sequence; shared-prefix: also each private suffix; mixed: also the chunks)
     rows = np.asarray(st.step_rows)
+    step_slots = np.asarray(st.step_slots, dtype=np.int64)
+    newest = None
+    only_newest = len(step_slots) == len(w.decode_seqs) and all(len(sl) == 1 for sl, _ in st.step_writes)
+    if args.append == "on" or (args.append == "auto" and only_newest):
+        # each decode sequence's newest token (position L - 1) goes in through
+        # the decode kernel; the step's other tokens (private suffixes, prefill
+        # chunks) through the cache write
+        new_slot, new_row = [], []
+        for i, s_ in enumerate(w.decode_seqs):
+            p = int(st.lens_host[i]) - 1
+            new_slot.append(int(st.tables_host[i][p // w.block_size]) * w.block_size + p % w.block_size)
+            new_row.append(int(w.tok_rows[s_][p]))
+        newest = {"k": lib_run.torch_stored(w.k_tok[new_row], w.dtype).cuda(),
+                  "v": lib_run.torch_stored(w.v_tok[new_row], w.dtype).cuda(),
+                  "slots": torch.tensor(new_slot, dtype=torch.int64, device="cuda")}
+        keep = ~np.isin(step_slots, np.asarray(new_slot, dtype=np.int64))
+        rows, step_slots = rows[keep], step_slots[keep]
     k_new = lib_run.torch_stored(w.k_tok[rows], w.dtype).cuda()
     v_new = lib_run.torch_stored(w.v_tok[rows], w.dtype).cuda()
-    slots = torch.from_numpy(np.ascontiguousarray(st.step_slots)).cuda()
+    slots = torch.from_numpy(np.ascontiguousarray(step_slots)).cuda()
     pairs = st.step_pairs
 
     pre = None
@@ -294,10 +317,15 @@ def main():
         if pairs:
             pa.pa_copy_blocks(kc, vc, st.desc, pairs)
         mark(1)
-        pa.pa_cache_write(kc, vc, st.desc, k_new, v_new, slots)
+        if slots.numel():
+            pa.pa_cache_write(kc, vc, st.desc, k_new, v_new, slots)
         mark(2)
-        pa.pa_decode_partitions(out, st.q, kc, vc, st.desc, st.tables, st.lens, max_ctx, w.scale,
-                                args.partition, ws)
+        if newest is not None:
+            pa.pa_decode_append_partitions(out, st.q, newest["k"], newest["v"], newest["slots"], kc, vc,
+                                           st.desc, st.tables, st.lens, max_ctx, w.scale, args.partition, ws)
+        else:
+            pa.pa_decode_partitions(out, st.q, kc, vc, st.desc, st.tables, st.lens, max_ctx, w.scale,
+                                    args.partition, ws)
         mark(3)
         pa.pa_decode_reduce(out, st.lens, Hq, D, max_ctx, args.partition, ws)
         mark(4)
@@ -374,8 +402,9 @@ def main():
                    "context_tokens": tokens, "q_heads": Hq, "kv_heads": H, "head_dim": D,
                    "block_size": w.block_size, "partition": args.partition, "pool_copies": copies,
                    "step": ("copy_blocks + " if pairs else "") +
-                           "cache_write + decode_partitions + decode_reduce" +
-                           (" + prefill" if pre is not None else "")},
+                           ("cache_write + " if slots.numel() else "") +
+                           ("decode_append_partitions" if newest is not None else "decode_partitions") +
+                           " + decode_reduce" + (" + prefill" if pre is not None else "")},
         "roofline": {"bound": "hbm", "kernel": "decode_partition_kernel", "achieved": achieved,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                      "traffic": load_traffic(args.workload), "algorithmic_bytes_per_launch": algo,
@@ -384,7 +413,8 @@ def main():
                      "kernel_source_hash": kernel_source_hash()},
         "decode_gbs_whole_step": algo / (ms_per_step / 1e3) / 1e9,
         "hip_graph_ms_per_step": graph_ms,
-        "kernels_us_untimed_pass": {"copy_blocks": avg_us(0, 1) if pairs else None, "cache_write": avg_us(1, 2),
+        "kernels_us_untimed_pass": {"copy_blocks": avg_us(0, 1) if pairs else None,
+                                    "cache_write": avg_us(1, 2) if slots.numel() else None,
                        "decode_partitions": avg_us(2, 3), "decode_reduce": avg_us(3, 4),
                        "prefill": avg_us(4, 5) if pre is not None else None},
     }

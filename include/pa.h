@@ -312,6 +312,44 @@ int pa_decode_reduce(void* out, int32_t out_dtype, const int32_t* context_lens, 
                      int32_t partition_size, void* workspace, size_t workspace_bytes,
                      void* stream);
 
+/* Decode with append: the decode step of sequences whose newest token
+ * (position context_lens[s] - 1) has just been produced, in one pass instead of
+ * pa_cache_write followed by pa_decode ([studynote 223] section II figure: the
+ * new token's KV goes into the block its table links in, and the request then
+ * attends over all its blocks).  The workgroup that attends over a sequence's
+ * last chunk first stores that token's K/V at slot_mapping[s] of the pools,
+ * then reads them back with the rest of the context.
+ *   k_new, v_new:  device [num_seqs][num_kv_heads][head_dim], cache dtype.
+ *   slot_mapping:  device int64 [num_seqs]: the slot the allocator gave position
+ *                  context_lens[s] - 1 of sequence s.  Negative: nothing is
+ *                  stored (as pa_cache_write, the attention then reads whatever
+ *                  the pool holds there); a slot >= num_blocks*block_size is
+ *                  ignored.
+ *   k_cache, v_cache: written at those slots, read everywhere.
+ * Other arguments, checks and results as pa_decode: the output and the pools
+ * equal those of pa_cache_write(k_new, v_new, slot_mapping) + pa_decode bit
+ * for bit, provided no row of the call reads a slot that another row stores
+ * (copy-on-write in the allocator guarantees this: a new token never lands in
+ * a block another sequence reads).
+ * PA_ERR_INVALID_ARG if k_new, v_new or slot_mapping is NULL with num_seqs > 0. */
+int pa_decode_append(void* out, int32_t out_dtype, const void* q, const void* k_new,
+                     const void* v_new, const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                     const pa_cache_desc* desc, const int32_t* block_tables,
+                     int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                     int32_t num_q_heads, int32_t max_context_len, float scale,
+                     int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream);
+
+/* First half of pa_decode_append (the split-K pass with the append); pair it
+ * with pa_decode_reduce as for pa_decode_partitions. */
+int pa_decode_append_partitions(void* out, int32_t out_dtype, const void* q, const void* k_new,
+                                const void* v_new, const int64_t* slot_mapping, void* k_cache,
+                                void* v_cache, const pa_cache_desc* desc,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, int32_t num_seqs,
+                                int32_t num_q_heads, int32_t max_context_len, float scale,
+                                int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
 /* Causal attention of prefill chunks over their paged context, the prefill half
  * of a continuous-batching step ([studynote 223] section IV checklist item 2;
  * [studynote 528] section II, continuous batching table).

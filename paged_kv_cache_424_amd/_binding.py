@@ -126,6 +126,10 @@ _DEC = [_vp, _i32, _vp, _vp, _vp, _PD, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _
 _sig("pa_decode", ctypes.c_int, *_DEC)
 _sig("pa_decode_partitions", ctypes.c_int, *_DEC)
 _sig("pa_decode_reduce", ctypes.c_int, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp)
+_DEC_APPEND = [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _PD, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _i32,
+               _vp, _sz, _vp]
+_sig("pa_decode_append", ctypes.c_int, *_DEC_APPEND)
+_sig("pa_decode_append_partitions", ctypes.c_int, *_DEC_APPEND)
 _sig("pa_prefill", ctypes.c_int, _vp, _i32, _vp, _vp, _vp, _PD, _vp, _i32, _vp, _vp, _i32, _i32,
      _i32, _i32, _f32, _vp)
 
@@ -375,6 +379,33 @@ def pa_decode_partitions(out, q, k_cache, v_cache, desc, block_tables, context_l
                                                    context_lens, max_context_len, scale,
                                                    partition_size, workspace, stream)),
            "pa_decode_partitions")
+
+
+def _append_args(out, q, k_new, v_new, slot_mapping, k_cache, v_cache, desc, block_tables,
+                 context_lens, max_context_len, scale, partition_size, workspace, stream):
+    d = _decode_args(out, q, k_cache, v_cache, desc, block_tables, context_lens, max_context_len,
+                     scale, partition_size, workspace, stream)
+    return d[:3] + (_dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(slot_mapping, "slot_mapping")) + d[3:]
+
+
+def pa_decode_append(out, q, k_new, v_new, slot_mapping, k_cache, v_cache, desc, block_tables,
+                     context_lens, max_context_len, scale, partition_size=0, workspace=None, stream=None):
+    """pa_cache_write of each sequence's newest token (k_new/v_new [B][Hkv][D] at
+    slot_mapping[s], int64 [B]) and pa_decode, in one pass."""
+    _check(_lib.pa_decode_append(*_append_args(out, q, k_new, v_new, slot_mapping, k_cache, v_cache,
+                                               desc, block_tables, context_lens, max_context_len,
+                                               scale, partition_size, workspace, stream)),
+           "pa_decode_append")
+
+
+def pa_decode_append_partitions(out, q, k_new, v_new, slot_mapping, k_cache, v_cache, desc,
+                                block_tables, context_lens, max_context_len, scale, partition_size=0,
+                                workspace=None, stream=None):
+    _check(_lib.pa_decode_append_partitions(*_append_args(out, q, k_new, v_new, slot_mapping, k_cache,
+                                                          v_cache, desc, block_tables, context_lens,
+                                                          max_context_len, scale, partition_size,
+                                                          workspace, stream)),
+           "pa_decode_append_partitions")
 
 
 def pa_decode_reduce(out, context_lens, num_q_heads, head_dim, max_context_len, partition_size=0,

@@ -98,6 +98,14 @@ struct DecodeArgs {
     float* ws_acc;     // [B][Hq][pmax][D]
     float2* ws_ml;     // [B][Hq][pmax] (max in log2 units, sum)
     int32_t* ws_np;    // [B][Hq] pieces of the (sequence, head)
+    // Decode with append (all null otherwise): the newest token (position L - 1)
+    // of sequence s has K/V k_new[s], v_new[s] ([B][H][D], cache dtype); they
+    // are used for that position and stored at slot new_slots[s] of kw / vw.
+    const void* k_new;
+    const void* v_new;
+    const int64_t* new_slots;
+    void* kw;
+    void* vw;
     int32_t B, Hq, H, G, bs, N, maxb, max_ctx;
     int32_t part_chunks;   // > 0: fixed partitions of this many 32-token chunks; 0: balanced
     int32_t pmax;          // piece slots per (sequence, head) in the workspace
@@ -186,7 +194,7 @@ struct ChunkRegs {
 
 // fp32 caches at head_dim 128 hold twice the registers per chunk and run at
 // two waves per SIMD; every other variant at three.
-template <bool BF16, int D, bool FIXED>
+template <bool BF16, int D, bool FIXED, bool APPEND>
 __global__ __launch_bounds__((64 * waves_per_group<BF16, D, FIXED>()))
 __attribute__((amdgpu_waves_per_eu((waves_per_simd<BF16, D>())))) void decode_partition_kernel(DecodeArgs a) {
     constexpr int NW = waves_per_group<BF16, D, FIXED>();   // waves per workgroup
@@ -231,6 +239,37 @@ __attribute__((amdgpu_waves_per_eu((waves_per_simd<BF16, D>())))) void decode_pa
         const char* vbase = static_cast<const char*>(a.vc) + static_cast<int64_t>(g) * D * bs * ES;
         const int nblk_seq = (L + bs - 1) / bs;
         const int32_t* trow = a.tables + static_cast<int64_t>(s) * a.maxb;
+        const int last_ci = (L - 1) / kChunk;     // chunk of the newest token
+        const char* knew = APPEND ? static_cast<const char*>(a.k_new) +
+                                        ((static_cast<int64_t>(s) * H + g) * D) * ES
+                                  : nullptr;
+        const char* vnew = APPEND ? static_cast<const char*>(a.v_new) +
+                                        ((static_cast<int64_t>(s) * H + g) * D) * ES
+                                  : nullptr;
+        // append: the piece that holds the newest token first stores that
+        // token's K/V in the pools (one channel per thread, D <= NT).  A
+        // workgroup-scope release before the first window's barrier and an
+        // acquire after it make the stores visible to this workgroup's loads,
+        // so the token is then read back like every other one.
+        const bool app_here = APPEND && ce > last_ci;
+        if constexpr (APPEND) {
+            if (app_here && tid < D) {
+                const int64_t slot = a.new_slots[s];
+                if (slot >= 0 && slot < static_cast<int64_t>(a.N) * bs) {
+                    const int64_t blk = slot / bs, off = slot % bs;
+                    const int d = tid;
+                    const int64_t kidx = (blk * H + g) * bs * D + ((d >> 5) * bs + off) * 32 + (d & 31);
+                    const int64_t vidx = ((blk * H + g) * D + d) * bs + off;
+                    if constexpr (BF16) {
+                        static_cast<uint16_t*>(a.kw)[kidx] = reinterpret_cast<const uint16_t*>(knew)[d];
+                        static_cast<uint16_t*>(a.vw)[vidx] = reinterpret_cast<const uint16_t*>(vnew)[d];
+                    } else {
+                        static_cast<uint32_t*>(a.kw)[kidx] = reinterpret_cast<const uint32_t*>(knew)[d];
+                        static_cast<uint32_t*>(a.vw)[vidx] = reinterpret_cast<const uint32_t*>(vnew)[d];
+                    }
+                }
+            }
+        }
 
         // Query operand: lane (j, r) holds head r's channels for k-group j.
         u32x4 qreg[QV];
@@ -404,7 +443,13 @@ __attribute__((amdgpu_waves_per_eu((waves_per_simd<BF16, D>())))) void decode_pa
                 }
                 ids[tid] = id;
             }
+            if constexpr (APPEND) {
+                if (app_here && wb == cb) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            }
             bad = __syncthreads_or(bad);
+            if constexpr (APPEND) {
+                if (app_here && wb == cb) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            }
             // Latency is hidden by occupancy (three waves per SIMD), not by a
             // register double buffer: holding a second chunk needs ~280
             // registers, which spills even at two waves per SIMD.
@@ -732,7 +777,11 @@ int device_cus(int* cus) {
 template <bool BF16, int D>
 int launch_partitions(const DecodeArgs& a0, int32_t num_seqs, const Plan& c, hipStream_t st) {
     const bool fixed = c.part_chunks > 0;
-    const auto kernel = fixed ? decode_partition_kernel<BF16, D, true> : decode_partition_kernel<BF16, D, false>;
+    const bool app = a0.k_new != nullptr;
+    const auto kernel = fixed ? (app ? decode_partition_kernel<BF16, D, true, true>
+                                     : decode_partition_kernel<BF16, D, true, false>)
+                              : (app ? decode_partition_kernel<BF16, D, false, true>
+                                     : decode_partition_kernel<BF16, D, false, false>);
     const int waves = fixed ? waves_per_group<BF16, D, true>() : waves_per_group<BF16, D, false>();
     int cus = 0;
     int rc = device_cus(&cus);
@@ -748,6 +797,11 @@ int launch_partitions(const DecodeArgs& a0, int32_t num_seqs, const Plan& c, hip
         a.q = static_cast<const char*>(a0.q) + static_cast<int64_t>(s0) * a0.Hq * D * ES;
         a.tables = a0.tables + static_cast<int64_t>(s0) * a0.maxb;
         a.lens = a0.lens + s0;
+        if (a0.k_new) {
+            a.k_new = static_cast<const char*>(a0.k_new) + static_cast<int64_t>(s0) * a0.H * D * ES;
+            a.v_new = static_cast<const char*>(a0.v_new) + static_cast<int64_t>(s0) * a0.H * D * ES;
+            a.new_slots = a0.new_slots + s0;
+        }
         if (a0.ws_np) {
             a.ws_acc = reinterpret_cast<float*>(reinterpret_cast<char*>(a0.ws_acc) + s0 * per_seq_acc);
             a.ws_ml = reinterpret_cast<float2*>(reinterpret_cast<char*>(a0.ws_ml) + s0 * per_seq_ml);
@@ -763,7 +817,10 @@ int launch_partitions(const DecodeArgs& a0, int32_t num_seqs, const Plan& c, hip
             // as many workgroups as the chip holds at once, and no more than
             // minimal ranges of the longest context could keep busy
             int per_cu = 0;
-            rc = hip_status(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64 * waves, lds));
+            // sized by the plain kernel even for the append variant, so that both
+            // cut the batch at the same points and round identically
+            rc = hip_status(hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &per_cu, decode_partition_kernel<BF16, D, false, false>, 64 * waves, lds));
             if (rc != PA_OK) return rc;
             if (per_cu < 1) return PA_ERR_UNSUPPORTED;
             const int64_t nch = (static_cast<int64_t>(a.max_ctx) + kChunk - 1) / kChunk;
@@ -791,13 +848,20 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
     return pa::workspace_layout(num_seqs, num_q_heads, head_dim, pmax, part_chunks > 0).total;
 }
 
-int pa_decode_partitions(void* out, int32_t out_dtype, const void* q, const void* k_cache,
-                         const void* v_cache, const pa_cache_desc* desc,
-                         const int32_t* block_tables, int32_t max_blocks_per_seq,
-                         const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
-                         int32_t max_context_len, float scale, int32_t partition_size,
-                         void* workspace, size_t workspace_bytes, void* stream) {
-    using namespace pa;
+}  // extern "C"
+
+namespace pa {
+namespace {
+
+// The split-K pass; with k_new non-null, also the append of each sequence's
+// newest token (kw/vw are then the writable pools).
+int decode_partitions(void* out, int32_t out_dtype, const void* q, const void* k_cache,
+                      const void* v_cache, const pa_cache_desc* desc, const int32_t* block_tables,
+                      int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                      int32_t num_q_heads, int32_t max_context_len, float scale,
+                      int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream,
+                      const void* k_new, const void* v_new, const int64_t* new_slots, void* kw,
+                      void* vw) {
     Plan c;
     int rc = check_decode(desc, out_dtype, num_seqs, num_q_heads, max_blocks_per_seq, max_context_len,
                           partition_size, &c);
@@ -820,6 +884,11 @@ int pa_decode_partitions(void* out, int32_t out_dtype, const void* q, const void
     a.ws_acc = ws.total ? reinterpret_cast<float*>(wsb + ws.acc) : nullptr;
     a.ws_ml = ws.total ? reinterpret_cast<float2*>(wsb + ws.ml) : nullptr;
     a.ws_np = ws.total ? reinterpret_cast<int32_t*>(wsb + ws.np) : nullptr;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.new_slots = new_slots;
+    a.kw = kw;
+    a.vw = vw;
     a.B = num_seqs;
     a.Hq = num_q_heads;
     a.H = desc->num_kv_heads;
@@ -839,6 +908,38 @@ int pa_decode_partitions(void* out, int32_t out_dtype, const void* q, const void
                         : launch_partitions<true, 64>(a, num_seqs, c, st);
     return D == 128 ? launch_partitions<false, 128>(a, num_seqs, c, st)
                     : launch_partitions<false, 64>(a, num_seqs, c, st);
+}
+
+}  // namespace
+}  // namespace pa
+
+extern "C" {
+
+int pa_decode_partitions(void* out, int32_t out_dtype, const void* q, const void* k_cache,
+                         const void* v_cache, const pa_cache_desc* desc,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                         int32_t max_context_len, float scale, int32_t partition_size,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    return pa::decode_partitions(out, out_dtype, q, k_cache, v_cache, desc, block_tables,
+                                 max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                                 max_context_len, scale, partition_size, workspace, workspace_bytes,
+                                 stream, nullptr, nullptr, nullptr, nullptr, nullptr);
+}
+
+int pa_decode_append_partitions(void* out, int32_t out_dtype, const void* q, const void* k_new,
+                                const void* v_new, const int64_t* slot_mapping, void* k_cache,
+                                void* v_cache, const pa_cache_desc* desc,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, int32_t num_seqs,
+                                int32_t num_q_heads, int32_t max_context_len, float scale,
+                                int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+    if (num_seqs > 0 && (!k_new || !v_new || !slot_mapping)) return PA_ERR_INVALID_ARG;
+    return pa::decode_partitions(out, out_dtype, q, k_cache, v_cache, desc, block_tables,
+                                 max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                                 max_context_len, scale, partition_size, workspace, workspace_bytes,
+                                 stream, k_new, v_new, slot_mapping, k_cache, v_cache);
 }
 
 int pa_decode_reduce(void* out, int32_t out_dtype, const int32_t* context_lens, int32_t num_seqs,
@@ -866,6 +967,21 @@ int pa_decode_reduce(void* out, int32_t out_dtype, const int32_t* context_lens, 
                          reinterpret_cast<const float*>(wsb + ws.acc),
                          reinterpret_cast<const float2*>(wsb + ws.ml),
                          reinterpret_cast<const int32_t*>(wsb + ws.np), pairs, pmax);
+}
+
+int pa_decode_append(void* out, int32_t out_dtype, const void* q, const void* k_new, const void* v_new,
+                     const int64_t* slot_mapping, void* k_cache, void* v_cache, const pa_cache_desc* desc,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                     int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len, float scale,
+                     int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = pa_decode_append_partitions(out, out_dtype, q, k_new, v_new, slot_mapping, k_cache, v_cache,
+                                         desc, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                                         num_q_heads, max_context_len, scale, partition_size, workspace,
+                                         workspace_bytes, stream);
+    if (rc != PA_OK) return rc;
+    return pa_decode_reduce(out, out_dtype, context_lens, num_seqs, num_q_heads,
+                            desc ? desc->head_dim : 0, max_context_len, partition_size, workspace,
+                            workspace_bytes, stream);
 }
 
 int pa_decode(void* out, int32_t out_dtype, const void* q, const void* k_cache, const void* v_cache,

@@ -104,6 +104,7 @@ def build(w, device="cuda", run_step=True):
             _write(st, w, [item], device)
     else:
         _write(st, w, writes["setup"], device)
+    st.step_writes = writes["step"]          # (slots, rows) of the step, in script order
     if run_step:
         if st.step_pairs:
             pa.pa_copy_blocks(st.kc, st.vc, st.desc, st.step_pairs)

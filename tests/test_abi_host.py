@@ -257,6 +257,18 @@ def test_device_calls_reject_bad_host_arguments():
     # partition sizes must be multiples of 32 tokens
     assert pa.pa_decode_workspace_bytes(2, 8, 128, 1000, 100) == 0
     assert dec(one, 0, one, one, one, ref(desc), one, 4, one, 2, 8, 64, 0.1, 48, None, 0, None) == pa.PA_ERR_UNSUPPORTED
+    # decode with append: the new tokens' K/V and their slots are required; the
+    # other checks are pa_decode's
+    app = lib.pa_decode_append
+    for missing in range(3):
+        kv = [one, one, one]
+        kv[missing] = None
+        assert app(one, 0, one, *kv, one, one, ref(desc), one, 4, one, 2, 8, 64, 0.1, 0, None, 0,
+                   None) == pa.PA_ERR_INVALID_ARG
+    assert app(one, 0, one, one, one, one, one, one, ref(desc), one, 4, one, 2, 34, 64, 0.1, 0, None, 0,
+               None) == pa.PA_ERR_UNSUPPORTED
+    assert app(one, 0, one, None, None, None, one, one, ref(desc), one, 4, one, 0, 8, 64, 0.1, 0, None, 0,
+               None) == pa.PA_OK                     # an empty batch needs nothing
 
 
 # ---- prefix caching: C++ vs oracle ------------------------------------------------------------
