@@ -60,6 +60,50 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
         dst[static_cast<int64_t>(d) * bs] = src[d];
 }
 
+// The same scatter with 16-byte accesses, for head_dim a multiple of 32 (K
+// rows then fall in whole 32-channel groups) and 16-byte-aligned buffers.  K:
+// each thread moves one 16-byte piece of a token row straight to its group row;
+// a wave moves four tokens, so consecutive slots give 256-byte runs.  V: the
+// group's rows are staged in LDS with 16-byte loads, then stored token-fastest
+// as in cache_write_kernel.  The slots are read once per workgroup.
+template <typename W>
+__global__ __launch_bounds__(256) void cache_write_vec_kernel(
+    W* __restrict__ kc, W* __restrict__ vc, const W* __restrict__ kn, const W* __restrict__ vn,
+    const int64_t* __restrict__ slots, int32_t num_tokens, int32_t H, int32_t D, int32_t bs,
+    int64_t num_slots) {
+    constexpr int EPV = 16 / sizeof(W);                    // elements per 16-byte piece
+    __shared__ int64_t s_slot[kGroupTokens];
+    __shared__ __align__(16) W s_v[kGroupTokens * 128 * 4 / sizeof(W)];   // D * sizeof(W) <= 512 bytes
+    const int g = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kGroupTokens;
+    const int nt = static_cast<int>(min(static_cast<int64_t>(kGroupTokens), num_tokens - t0));
+    const int pieces = D / EPV;                            // per token row
+    if (tid < nt) s_slot[tid] = slots[t0 + tid];
+    for (int e = tid; e < nt * pieces; e += 256) {
+        const int i = e / pieces, p = e % pieces;
+        *reinterpret_cast<uint4*>(&s_v[i * D + p * EPV]) =
+            *reinterpret_cast<const uint4*>(&vn[((t0 + i) * H + g) * D + p * EPV]);
+    }
+    __syncthreads();
+    for (int e = tid; e < nt * pieces; e += 256) {
+        const int i = e / pieces, p = e % pieces;
+        const int64_t slot = s_slot[i];
+        if (slot < 0 || slot >= num_slots) continue;
+        const int64_t blk = slot / bs, off = slot % bs;
+        const int d0 = p * EPV;
+        W* dst = kc + (blk * H + g) * bs * D + ((d0 >> 5) * static_cast<int64_t>(bs) + off) * 32 + (d0 & 31);
+        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(&kn[((t0 + i) * H + g) * D + d0]);
+    }
+    const int i = tid % kGroupTokens;
+    if (i >= nt) return;
+    const int64_t slot = s_slot[i];
+    if (slot < 0 || slot >= num_slots) return;
+    const int64_t blk = slot / bs, off = slot % bs;
+    W* dst = vc + (blk * H + g) * D * static_cast<int64_t>(bs) + off;
+    for (int d = tid / kGroupTokens; d < D; d += 256 / kGroupTokens) dst[static_cast<int64_t>(d) * bs] = s_v[i * D + d];
+}
+
 constexpr int kPairsPerLaunch = 128;
 
 struct CopyBatch {
@@ -100,6 +144,19 @@ int pa_cache_write(void* k_cache, void* v_cache, const pa_cache_desc* desc, cons
     if (groups > INT32_MAX || H > 65535) return PA_ERR_UNSUPPORTED;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const dim3 grid(static_cast<uint32_t>(groups), static_cast<uint32_t>(H));
+    const bool aligned = ((reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache) |
+                           reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15) == 0;
+    if (aligned && D % 32 == 0 && D <= 128) {
+        if (desc->kv_dtype == PA_BF16)
+            return launch_kernel(cache_write_vec_kernel<uint16_t>, grid, dim3(256), 0, st,
+                                 static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
+                                 static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+                                 slot_mapping, num_tokens, H, D, bs, num_slots);
+        return launch_kernel(cache_write_vec_kernel<uint32_t>, grid, dim3(256), 0, st,
+                             static_cast<uint32_t*>(k_cache), static_cast<uint32_t*>(v_cache),
+                             static_cast<const uint32_t*>(k_new), static_cast<const uint32_t*>(v_new),
+                             slot_mapping, num_tokens, H, D, bs, num_slots);
+    }
     if (desc->kv_dtype == PA_BF16)
         return launch_kernel(cache_write_kernel<uint16_t>, grid, dim3(256), 0, st,
                              static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),

@@ -622,17 +622,31 @@ __global__ __launch_bounds__(64 * kReduceWaves) void decode_reduce_kernel(void* 
                                                                          const int32_t* __restrict__ ws_np,
                                                                          int64_t pairs, int32_t P) {
     constexpr int CPL = D / 64;                   // channels per lane
+    constexpr int kPre = 4;                       // partial rows loaded before the piece count
     const int lane = threadIdx.x & 63;
     const int64_t pair = static_cast<int64_t>(blockIdx.x) * kReduceWaves + (threadIdx.x >> 6);
     if (pair >= pairs) return;
-    const int np = min(ws_np[pair], P);
-    if (np <= 1) return;                          // final already, or NaN written
+    // The piece count, the first 64 (max, sum) pairs and the first kPre partial
+    // rows are loaded together, before the count is known, so a head with few
+    // pieces costs one round trip to memory.  All those slots lie inside the
+    // workspace; the ones past the count hold leftovers and are never used
+    // (selected away, not multiplied by zero, as they may be NaN).
+    const int np_raw = ws_np[pair];
     const float2* ml = ws_ml + pair * P;
-    float m = -INFINITY;
-    for (int i = lane; i < np; i += 64) m = fmaxf(m, ml[i].x);
+    const float2 ml0 = lane < P ? ml[lane] : make_float2(-INFINITY, 0.f);
+    const float* accp = ws_acc + pair * P * D + lane;
+    float pre[kPre][CPL];
+#pragma unroll
+    for (int u = 0; u < kPre; ++u)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) pre[u][c] = u < P ? accp[static_cast<int64_t>(u) * D + 64 * c] : 0.f;
+    const int np = min(np_raw, P);
+    if (np <= 1) return;                          // final already, or NaN written
+    float m = lane < np ? ml0.x : -INFINITY;
+    for (int i = lane + 64; i < np; i += 64) m = fmaxf(m, ml[i].x);
     const float M = wave_max(m);
-    float dp = 0.f;
-    for (int i = lane; i < np; i += 64) {
+    float dp = lane < np ? __builtin_amdgcn_exp2f(ml0.x - M) * ml0.y : 0.f;
+    for (int i = lane + 64; i < np; i += 64) {
         const float2 v = ml[i];
         dp += __builtin_amdgcn_exp2f(v.x - M) * v.y;
     }
@@ -640,7 +654,6 @@ __global__ __launch_bounds__(64 * kReduceWaves) void decode_reduce_kernel(void* 
     // Each lane computes the weight of one piece of a block of 64; the weights
     // are broadcast with shuffles and the channel sums are kept in four
     // independent accumulators, so four loads per lane are in flight.
-    const float* accp = ws_acc + pair * P * D + lane;
     float o[4][CPL];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
@@ -648,8 +661,17 @@ __global__ __launch_bounds__(64 * kReduceWaves) void decode_reduce_kernel(void* 
         for (int c = 0; c < CPL; ++c) o[u][c] = 0.f;
     for (int b0 = 0; b0 < np; b0 += 64) {
         const int nb = min(64, np - b0);
-        const float fl = lane < nb ? __builtin_amdgcn_exp2f(ml[b0 + lane].x - M) : 0.f;
+        const float fl = lane < nb ? __builtin_amdgcn_exp2f((b0 == 0 ? ml0.x : ml[b0 + lane].x) - M) : 0.f;
         int k = 0;
+        if (b0 == 0) {
+#pragma unroll
+            for (int u = 0; u < kPre; ++u) {
+                const float f = __shfl(fl, u);
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) o[u][c] += u < nb ? f * pre[u][c] : 0.f;
+            }
+            k = kPre;
+        }
         for (; k + 4 <= nb; k += 4) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {

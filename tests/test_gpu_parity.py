@@ -355,16 +355,18 @@ def test_negative_slots_are_padding():
     assert np.array_equal(before_k, lib_run.pool_bits(st.kc, w.dtype))
 
 
-@pytest.mark.parametrize("dtype,bs", [("bf16", 16), ("bf16", 8), ("bf16", 32), ("f32", 16), ("bf16", 12)])
-def test_cache_write_runs_and_scattered_slots(dtype, bs):
-    # aligned runs of 8 consecutive slots take the 16-byte store path; runs off
-    # by one slot, runs crossing a block, padding inside a run and scattered
-    # slots take the element path; the pools must match the oracle's bit for bit
+@pytest.mark.parametrize("dtype,bs,D", [("bf16", 16, 64), ("bf16", 8, 128), ("bf16", 32, 64), ("f32", 16, 64),
+                                        ("f32", 8, 128), ("bf16", 12, 64), ("bf16", 16, 48), ("f32", 16, 40)])
+def test_cache_write_runs_and_scattered_slots(dtype, bs, D):
+    # runs of consecutive slots (aligned, off by one, crossing a block, with
+    # padding inside) and scattered slots, on the 16-byte path (head_dim a
+    # multiple of 32) and the element path (48, 40); the pools must match the
+    # oracle's bit for bit
     import paged_kv_cache_424_amd as pa
     from oracle import cache
-    _announce(f"cache_write runs {dtype} bs={bs}")
-    rng = np.random.default_rng(bs)
-    H, D, N = 4, 64, 24
+    _announce(f"cache_write runs {dtype} bs={bs} D={D}")
+    rng = np.random.default_rng(bs + D)
+    H, N = 4, 24
     nslots = N * bs
     slots = []
     slots += list(range(0, 8))                       # aligned run
