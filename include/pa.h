@@ -263,6 +263,7 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  * 0..context_lens[s]-1 of kv head h / (num_q_heads / num_kv_heads).
  *   out:          device [num_seqs][num_q_heads][head_dim] of out_dtype (PA_F32 or PA_BF16).
  *   q:            device [num_seqs][num_q_heads][head_dim] in the cache dtype.
+ *   q, k_cache, v_cache: 16-byte aligned (PA_ERR_INVALID_ARG otherwise).
  *   block_tables: device int32 [num_seqs][max_blocks_per_seq]; only the first
  *                 ceil(L/block_size) entries of a row are read.
  *   context_lens: device int32 [num_seqs]; L counts the newest token.
@@ -316,10 +317,12 @@ int pa_decode_reduce(void* out, int32_t out_dtype, const int32_t* context_lens, 
  * (position context_lens[s] - 1) has just been produced, in one pass instead of
  * pa_cache_write followed by pa_decode ([studynote 223] section II figure: the
  * new token's KV goes into the block its table links in, and the request then
- * attends over all its blocks).  The workgroup that attends over a sequence's
- * last chunk first stores that token's K/V at slot_mapping[s] of the pools,
- * then reads them back with the rest of the context.
- *   k_new, v_new:  device [num_seqs][num_kv_heads][head_dim], cache dtype.
+ * attends over all its blocks).  The newest tokens are stored at
+ * slot_mapping[s] of the pools by the workgroups that attend over the
+ * sequences' last chunks, which then read them back with the rest of the
+ * context (a workgroup-scope release/acquire orders the two).
+ *   k_new, v_new:  device [num_seqs][num_kv_heads][head_dim], cache dtype,
+ *                  aligned to their element.
  *   slot_mapping:  device int64 [num_seqs]: the slot the allocator gave position
  *                  context_lens[s] - 1 of sequence s.  Negative: nothing is
  *                  stored (as pa_cache_write, the attention then reads whatever
@@ -330,8 +333,10 @@ int pa_decode_reduce(void* out, int32_t out_dtype, const int32_t* context_lens, 
  * equal those of pa_cache_write(k_new, v_new, slot_mapping) + pa_decode bit
  * for bit, provided no row of the call reads a slot that another row stores
  * (copy-on-write in the allocator guarantees this: a new token never lands in
- * a block another sequence reads).
- * PA_ERR_INVALID_ARG if k_new, v_new or slot_mapping is NULL with num_seqs > 0. */
+ * a block another sequence reads).  A row whose context length is invalid
+ * (NaN output) stores nothing.
+ * PA_ERR_INVALID_ARG if k_new, v_new or slot_mapping is NULL with num_seqs > 0,
+ * or misaligned. */
 int pa_decode_append(void* out, int32_t out_dtype, const void* q, const void* k_new,
                      const void* v_new, const int64_t* slot_mapping, void* k_cache, void* v_cache,
                      const pa_cache_desc* desc, const int32_t* block_tables,

@@ -232,6 +232,33 @@ __attribute__((amdgpu_waves_per_eu((waves_per_simd<BF16, D>())))) void decode_pa
     const int64_t tile_elems = static_cast<int64_t>(H) * bs * D;   // one block, all heads
     int buf = 0;                                                    // s_blk buffer in use
 
+    // Decode with append: store the newest token (position L - 1) of (sequence
+    // s, kv head g) at slot new_slots[s] of the pools, one channel per thread
+    // (D <= NT).  Slots outside the pool store nothing.
+    auto store_newest = [&](int s, int g) {
+        if (tid >= D) return;
+        const int64_t slot = a.new_slots[s];
+        if (slot < 0 || slot >= static_cast<int64_t>(a.N) * bs) return;
+        const int64_t src = (static_cast<int64_t>(s) * H + g) * D + tid;
+        const int64_t blk = slot / bs, off = slot % bs;
+        const int d = tid;
+        const int64_t kidx = (blk * H + g) * bs * D + ((d >> 5) * bs + off) * 32 + (d & 31);
+        const int64_t vidx = ((blk * H + g) * D + d) * bs + off;
+        if constexpr (BF16) {
+            static_cast<uint16_t*>(a.kw)[kidx] = static_cast<const uint16_t*>(a.k_new)[src];
+            static_cast<uint16_t*>(a.vw)[vidx] = static_cast<const uint16_t*>(a.v_new)[src];
+        } else {
+            static_cast<uint32_t*>(a.kw)[kidx] = static_cast<const uint32_t*>(a.k_new)[src];
+            static_cast<uint32_t*>(a.vw)[vidx] = static_cast<const uint32_t*>(a.v_new)[src];
+        }
+    };
+    // Set once this workgroup has stored newest tokens that it reads back: the
+    // next window barrier then carries a workgroup-scope release before it and
+    // an acquire after it, which make the stores visible to the workgroup's
+    // loads.  Fencing at that barrier rather than right after the stores lets
+    // the window's block-id loads overlap the wait for the stores.
+    bool fence_pending = false;
+
     // One partition: chunks [cb, ce) of (sequence s, kv head g), the piece-th
     // of its npieces partitions.
     auto process = [&](int s, int g, int L, int cb, int ce, int piece, int npieces) {
@@ -239,35 +266,14 @@ __attribute__((amdgpu_waves_per_eu((waves_per_simd<BF16, D>())))) void decode_pa
         const char* vbase = static_cast<const char*>(a.vc) + static_cast<int64_t>(g) * D * bs * ES;
         const int nblk_seq = (L + bs - 1) / bs;
         const int32_t* trow = a.tables + static_cast<int64_t>(s) * a.maxb;
-        const int last_ci = (L - 1) / kChunk;     // chunk of the newest token
-        const char* knew = APPEND ? static_cast<const char*>(a.k_new) +
-                                        ((static_cast<int64_t>(s) * H + g) * D) * ES
-                                  : nullptr;
-        const char* vnew = APPEND ? static_cast<const char*>(a.v_new) +
-                                        ((static_cast<int64_t>(s) * H + g) * D) * ES
-                                  : nullptr;
-        // append: the piece that holds the newest token first stores that
-        // token's K/V in the pools (one channel per thread, D <= NT).  A
-        // workgroup-scope release before the first window's barrier and an
-        // acquire after it make the stores visible to this workgroup's loads,
-        // so the token is then read back like every other one.
-        const bool app_here = APPEND && ce > last_ci;
-        if constexpr (APPEND) {
-            if (app_here && tid < D) {
-                const int64_t slot = a.new_slots[s];
-                if (slot >= 0 && slot < static_cast<int64_t>(a.N) * bs) {
-                    const int64_t blk = slot / bs, off = slot % bs;
-                    const int d = tid;
-                    const int64_t kidx = (blk * H + g) * bs * D + ((d >> 5) * bs + off) * 32 + (d & 31);
-                    const int64_t vidx = ((blk * H + g) * D + d) * bs + off;
-                    if constexpr (BF16) {
-                        static_cast<uint16_t*>(a.kw)[kidx] = reinterpret_cast<const uint16_t*>(knew)[d];
-                        static_cast<uint16_t*>(a.vw)[vidx] = reinterpret_cast<const uint16_t*>(vnew)[d];
-                    } else {
-                        static_cast<uint32_t*>(a.kw)[kidx] = reinterpret_cast<const uint32_t*>(knew)[d];
-                        static_cast<uint32_t*>(a.vw)[vidx] = reinterpret_cast<const uint32_t*>(vnew)[d];
-                    }
-                }
+        // Fixed partitions: the piece that holds the newest token stores it
+        // first and then reads it back like every other token.  (The balanced
+        // split stores all of a workgroup's newest tokens before its first
+        // piece.)
+        if constexpr (APPEND && FIXED) {
+            if (ce > (L - 1) / kChunk) {
+                store_newest(s, g);
+                fence_pending = true;
             }
         }
 
@@ -444,11 +450,12 @@ __attribute__((amdgpu_waves_per_eu((waves_per_simd<BF16, D>())))) void decode_pa
                 ids[tid] = id;
             }
             if constexpr (APPEND) {
-                if (app_here && wb == cb) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+                if (fence_pending) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
             }
             bad = __syncthreads_or(bad);
             if constexpr (APPEND) {
-                if (app_here && wb == cb) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+                if (fence_pending) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+                fence_pending = false;
             }
             // Latency is hidden by occupancy (three waves per SIMD), not by a
             // register double buffer: holding a second chunk needs ~280
@@ -580,6 +587,24 @@ __attribute__((amdgpu_waves_per_eu((waves_per_simd<BF16, D>())))) void decode_pa
     const int64_t end = min(T, pos + Cw);
     if (pos >= end) return;
     int s = find_seq(s_cum, B, static_cast<int>(pos / H));
+    if constexpr (APPEND) {
+        // The range holds the last chunk of every (sequence, head) it ends
+        // inside: store those newest tokens before the first piece, outside the
+        // piece loop, so that loop keeps the plain kernel's registers.
+        int64_t p2 = pos;
+        int s2 = s;
+        while (p2 < end) {
+            const int n = s_cum[s2 + 1] - s_cum[s2];
+            const int64_t base = static_cast<int64_t>(H) * s_cum[s2];
+            const int g = static_cast<int>((p2 - base) / n);
+            const int off = static_cast<int>((p2 - base) % n);
+            const int take = static_cast<int>(min(static_cast<int64_t>(n - off), end - p2));
+            if (off + take == n) store_newest(s2, g);
+            p2 += take;
+            while (s2 < B && p2 >= static_cast<int64_t>(H) * s_cum[s2 + 1]) ++s2;
+        }
+        fence_pending = true;
+    }
     while (pos < end) {
         const int n = s_cum[s + 1] - s_cum[s];          // chunks per head of sequence s
         const int64_t base = static_cast<int64_t>(H) * s_cum[s];
@@ -890,6 +915,12 @@ int decode_partitions(void* out, int32_t out_dtype, const void* q, const void* k
     if (rc != PA_OK) return rc;
     if (num_seqs == 0) return PA_OK;
     if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
+    // 16-byte loads of q and the pools; element accesses of k_new and v_new
+    const uintptr_t esize = desc->kv_dtype == PA_BF16 ? 2 : 4;
+    if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) |
+         reinterpret_cast<uintptr_t>(v_cache)) % 16 ||
+        (reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) % esize)
+        return PA_ERR_INVALID_ARG;
     const int32_t D = desc->head_dim;
     const WsLayout ws = workspace_layout(num_seqs, num_q_heads, D, c.pmax, c.part_chunks > 0);
     if (ws.total > 0 && (!workspace || workspace_bytes < ws.total || reinterpret_cast<uintptr_t>(workspace) % 8))

@@ -269,6 +269,18 @@ def test_device_calls_reject_bad_host_arguments():
                None) == pa.PA_ERR_UNSUPPORTED
     assert app(one, 0, one, None, None, None, one, one, ref(desc), one, 4, one, 0, 8, 64, 0.1, 0, None, 0,
                None) == pa.PA_OK                     # an empty batch needs nothing
+    # 16-byte loads: q and the pools must be 16-byte aligned; k_new and v_new aligned to their element
+    odd8 = ctypes.c_void_p(24)
+    for i in range(3):
+        ptrs = [one, one, one]
+        ptrs[i] = odd8
+        assert dec(one, 0, ptrs[0], ptrs[1], ptrs[2], ref(desc), one, 4, one, 2, 8, 64, 0.1, 0, None, 0,
+                   None) == pa.PA_ERR_INVALID_ARG
+    for i in range(2):
+        kv = [one, one]
+        kv[i] = ctypes.c_void_p(17)
+        assert app(one, 0, one, *kv, one, one, one, ref(desc), one, 4, one, 2, 8, 64, 0.1, 0, None, 0,
+                   None) == pa.PA_ERR_INVALID_ARG
 
 
 # ---- prefix caching: C++ vs oracle ------------------------------------------------------------

@@ -3,9 +3,10 @@ pa_cache_write of each sequence's newest token followed by pa_decode.
 
 Both the outputs and the pools must be identical bit for bit: the fused path
 stores each newest token inside the decode kernel and reads it back with the
-rest of the context.  Also checked: a negative slot stores nothing (as in
-pa_cache_write), batches above one launch's 1,024 sequences, both partition
-modes and both cache dtypes.
+rest of the context.  Also checked: a negative slot stores
+nothing (as in pa_cache_write); a valid slot that is not the table's slot of
+the newest position is stored there and not read; batches above one launch's 1,024
+sequences; both partition modes and both cache dtypes.
 """
 
 import numpy as np
@@ -111,3 +112,49 @@ def test_append_graph_replays_match_eager():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, eager), rep
+
+
+@pytest.mark.parametrize("dtype,D,G,bs", [("bf16", 128, 3, 8), ("bf16", 64, 16, 128), ("f32", 64, 5, 32),
+                                          ("f32", 128, 1, 256)])
+def test_append_shapes(dtype, D, G, bs):
+    # other head groups, head sizes, cache dtypes and block sizes; lengths that
+    # put the newest token first, last and inside a block and a 32-token chunk
+    _announce(f"decode append shapes {dtype} D={D} G={G} bs={bs}")
+    lens = [1, 2, bs, bs + 1, 32, 33, 511, 512, 513, 1000]
+    w = workloads.decode_batch(seed=G + bs, lens=lens, name="app", Hq=2 * G, Hkv=2, D=D, bs=bs, dtype=dtype)
+    ref_st = lib_run.build(w)
+    st = lib_run.build(w, run_step=False)
+    k_new, v_new, slots = _new_tokens(w, st)
+    for part in (512, 0, 32):
+        ref = lib_run.decode(w, ref_st, partition_size=part)
+        got = _fused(w, st, part, k_new, v_new, slots)
+        assert torch.equal(got, ref), part
+    for a, b in ((st.kc, ref_st.kc), (st.vc, ref_st.vc)):
+        assert np.array_equal(lib_run.pool_bits(a, w.dtype), lib_run.pool_bits(b, w.dtype))
+
+
+@pytest.mark.parametrize("part", [512, 0])
+def test_slot_elsewhere_is_stored_not_read(part):
+    # every other sequence's newest token goes to a slot of a block no table
+    # holds: pa_cache_write + pa_decode then stores it there and reads the
+    # table's slot of the newest position (still the NaN sentinel), so those
+    # rows are NaN; the fused call must match that bit for bit
+    _announce(f"decode append, slots outside the tables, partition {part}")
+    w = workloads.make("c2", small=True)
+    ref_st = lib_run.build(w, run_step=False)
+    st = lib_run.build(w, run_step=False)
+    k_new, v_new, slots = _new_tokens(w, st)
+    bs, N = w.block_size, w.num_blocks
+    used = set(int(b) for b in st.tables.cpu().numpy().ravel() if b >= 0)
+    free = [b for b in range(N) if b not in used]
+    assert len(free) * bs >= len(slots) // 2
+    moved = slots.clone()
+    for i, s_ in enumerate(range(0, len(slots), 2)):
+        moved[s_] = free[i // bs] * bs + i % bs
+    pa.pa_cache_write(ref_st.kc, ref_st.vc, ref_st.desc, k_new, v_new, moved)
+    ref = lib_run.decode(w, ref_st, partition_size=part)
+    got = _fused(w, st, part, k_new, v_new, moved)
+    assert np.array_equal(got.cpu().numpy().view(np.uint32), ref.cpu().numpy().view(np.uint32))
+    assert torch.isnan(got[0::2]).all() and not torch.isnan(got[1::2]).any()
+    for a, b in ((st.kc, ref_st.kc), (st.vc, ref_st.vc)):
+        assert np.array_equal(lib_run.pool_bits(a, w.dtype), lib_run.pool_bits(b, w.dtype))
