@@ -45,6 +45,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kWaves = 4;
@@ -55,8 +57,6 @@ constexpr int kD = 128;
 constexpr int kKS = kD / 16;              // k-steps of the logits MFMA (16 channels each)
 constexpr int kMT = kD / 32;              // 32-channel tiles of the output
 constexpr int kKB = kKT / 16;             // 16-key blocks of the value MFMA
-constexpr int kKStride = kD + 8;          // bf16 per K row in LDS (272 bytes)
-constexpr int kVStride = kKT + 8;         // bf16 per V channel row in LDS (144 bytes)
 constexpr int kMinBlock = 8;
 constexpr int kIdsPerTile = kKT / kMinBlock;   // block ids one tile can touch
 constexpr float kLazyLog2 = 8.f;          // raise the running max only when it grows by > 2^8
@@ -89,6 +89,29 @@ __device__ __forceinline__ u32x4 keep_first_bf16(u32x4 v, int n) {
 
 constexpr u32x4 kZero4 = {0u, 0u, 0u, 0u};
 
+// 16 bytes per lane from global memory straight into LDS: lane i's bytes go
+// to dst + 16 i (dst is the same for the whole wave, passed in m0).  Written
+// as inline assembly on purpose: the compiler's form of this load makes it
+// wait for the load before the next LDS read of any buffer, which would
+// serialise the prefetch of tile t + 1 with the math of tile t.  The caller
+// waits for vmcnt to reach zero and then for a barrier before the data is
+// read.
+__device__ __forceinline__ void load_to_lds(const char* src, uint16_t* dst) {
+    const uint32_t lds_addr = __builtin_amdgcn_readfirstlane(
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)dst)));
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds_addr) : "memory", "m0");
+}
+constexpr bf16x2_t kOnes2 = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+
+// x of lane (l + 32) mod 64: one lane swap between the wave's halves.  After
+// v_permlane32_swap of (x, x) the first result holds the low half's values in
+// both halves and the second the high half's.
+__device__ __forceinline__ float other_half(float x) {
+    const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const int lane = threadIdx.x & 63;
+    return __uint_as_float(lane < 32 ? pr[1] : pr[0]);
+}
+
 // Key (within a 32-key MFMA tile) whose K row feeds A-operand row r: rows
 // r = 8j + 4h + i take key 16 (j / 2) + 8 h + 4 (j % 2) + i, so that output
 // element e of lane (h = lane / 32) holds key 16 (e / 8) + 8 h + e % 8.
@@ -99,9 +122,14 @@ __device__ __forceinline__ int k_row_key(int r) {
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(
     PrefillArgs a) {
-    __shared__ __align__(16) uint16_t sK[2][kKT * kKStride];
-    __shared__ __align__(16) uint16_t sV[2][kD * kVStride];
-    __shared__ int s_ids[2][kIdsPerTile];
+    // K tile [key][channel], rows of 256 bytes: 16-byte segment s of row r
+    // sits at position s ^ (r & 15).  V tile [channel][key], rows of 128
+    // bytes: segment s of row d sits at position s ^ ((d >> 1) & 7).  The
+    // swizzles put the 16 rows a quarter-wave reads at one segment on 16
+    // different bank groups.
+    __shared__ __align__(16) uint16_t sK[2][kKT * kD];
+    __shared__ __align__(16) uint16_t sV[2][kD * kKT];
+    __shared__ int64_t s_off[2][kIdsPerTile];   // byte offsets (id * tile bytes) of a tile's blocks
     __shared__ int s_order[kMaxSortedChunks];
 
     // ---- which (chunk, kv head, query tile) this workgroup takes ----
@@ -208,63 +236,46 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         return checked(b, raw_block_id(b));
     };
 
-    // ---- tile loader: each thread moves 4 K segments and 4 V segments of 16 bytes ----
-    // K segment p: key (tid / 16) + 16 p of the tile, channels 8 (tid % 16) ..
-    // +7, which sit in 32-channel group (tid % 16) / 4 of the block: the four
-    // keys of a quarter-wave are adjacent 64-byte rows of that group.  V
-    // segment p: channel (tid / 8) + 32 p, keys 8 (tid % 8) .. +7 (one block,
-    // as block_size >= 8).  With block_size <= 64 a tile starts on a
-    // block boundary, so a segment's block slot and in-block offset are the
-    // same for every tile and are computed once here; larger blocks add the
-    // tile's offset inside its block.
+    // ---- tile loader: global -> LDS directly (no registers), 16 bytes per lane ----
+    // Such a load writes its wave's 64 segments to 64 consecutive LDS
+    // segments, so the swizzle is applied by choosing which global segment
+    // each lane fetches.  K: load p of wave w fills rows 16 w + 4 p .. +3
+    // (lane / 16 picks the row, lane % 16 the position); V: load p of wave w
+    // fills channel rows 32 w + 8 p .. +7 (lane / 8 the row, lane % 8 the
+    // position).  A K segment (8 channels of one key) lies in one 32-channel
+    // group of its block, a V segment (8 keys of one channel) in one block,
+    // as block_size >= 8.  With block_size <= 64 a tile starts on a block
+    // boundary, so each segment's block slot and in-block offset are the same
+    // for every tile and are computed once here; larger blocks add the tile's
+    // offset inside its block.
     const int log2bs = a.log2bs;
     const bool big_blocks = bs > kKT;
     const int64_t tile_bytes = static_cast<int64_t>(a.H) * bs * kD * 2;
     const char* kbase = reinterpret_cast<const char*>(a.kc) + static_cast<int64_t>(g) * bs * kD * 2;
     const char* vbase = reinterpret_cast<const char*>(a.vc) + static_cast<int64_t>(g) * kD * bs * 2;
-    int kslot[4], koff[4];
+    int kslot[4], koff[4], vslot[4], voff[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        const int key = (tid >> 4) + 16 * p;
+        const int key = 16 * w + 4 * p + (lane >> 4);
+        const int seg = (lane & 15) ^ (key & 15);              // channels 8 seg .. +7
         kslot[p] = big_blocks ? 0 : key >> log2bs;
-        const int grp = (tid & 15) >> 2;                       // 32-channel group
-        koff[p] = ((grp * bs + (big_blocks ? key : key & (bs - 1))) * 32 + (tid & 3) * 8) * 2;   // bytes
+        koff[p] = (((seg >> 2) * bs + (big_blocks ? key : key & (bs - 1))) * 32 + (seg & 3) * 8) * 2;
+        const int d = 32 * w + 8 * p + (lane >> 3);
+        const int vkey = 8 * ((lane & 7) ^ ((d >> 1) & 7));    // keys vkey .. +7
+        vslot[p] = big_blocks ? 0 : vkey >> log2bs;
+        voff[p] = (d * bs + (big_blocks ? vkey : vkey & (bs - 1))) * 2;
     }
-    const int vkey = 8 * (tid & 7);
-    const int vslot = big_blocks ? 0 : vkey >> log2bs;
-    const int voff = (((tid >> 3) * bs) + (big_blocks ? vkey : vkey & (bs - 1))) * 2;  // bytes, p = 0
-    const int vstep = 32 * bs * 2;                                                   // bytes per p
-    u32x4 pk[4], pv[4];
-    auto load_tile = [&](int t, const int* ids) {
-        const int base = t * kKT;
+    // offs: the byte offsets of the tile's blocks, kept in LDS so that no
+    // thread multiplies a block id by the block's size
+    auto load_tile = [&](int t, const int64_t* offs, int buf) {
         // the tile's offset inside its block (only for blocks larger than a tile)
-        const int in_blk = big_blocks ? (base & (bs - 1)) : 0;
+        const int in_blk = big_blocks ? ((t * kKT) & (bs - 1)) : 0;
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const char* src = kbase + ids[kslot[p]] * tile_bytes + koff[p] + in_blk * 32 * 2;
-            pk[p] = *reinterpret_cast<const u32x4*>(src);
-        }
-        const char* vsrc = vbase + ids[vslot] * tile_bytes + voff + in_blk * 2;
+        for (int p = 0; p < 4; ++p)
+            load_to_lds(kbase + offs[kslot[p]] + koff[p] + in_blk * 32 * 2, &sK[buf][(16 * w + 4 * p) * kD]);
 #pragma unroll
-        for (int p = 0; p < 4; ++p) pv[p] = *reinterpret_cast<const u32x4*>(vsrc + p * vstep);
-        if (base + kKT > Lc) {
-            // values past the context are zeroed (a weight of 0 does not cancel a NaN)
-            const int nval = Lc - (base + vkey);
-#pragma unroll
-            for (int p = 0; p < 4; ++p) pv[p] = keep_first_bf16(pv[p], nval);
-        }
-    };
-    auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int key = (tid >> 4) + 16 * p, seg = tid & 15;
-            *reinterpret_cast<u32x4*>(&sK[buf][key * kKStride + seg * 8]) = pk[p];
-        }
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int d = (tid >> 3) + 32 * p, sg = tid & 7;
-            *reinterpret_cast<u32x4*>(&sV[buf][d * kVStride + 8 * sg]) = pv[p];
-        }
+        for (int p = 0; p < 4; ++p)
+            load_to_lds(vbase + offs[vslot[p]] + voff[p] + in_blk * 2, &sV[buf][(32 * w + 8 * p) * kKT]);
     };
     f32x16_t acc[kMT];
 #pragma unroll
@@ -277,21 +288,39 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const float lazy = kLazyLog2 / cscale;        // max growth tolerated before a rescale (raw units)
     const int wave_min_pos = P0 + qt * QT + ((32 * w) >> a.log2G);
     const int krow0 = k_row_key(col);             // K row read for A-operand row `col`
+    const int kx = krow0 & 15;                    // K swizzle of the rows this lane reads
+    const int vx = (col >> 1) & 7;                // V swizzle of the rows this lane reads
+    // The direct loads count in vmcnt; a wave's loads have written LDS once it
+    // reaches zero (encoding: vmcnt 0, expcnt and lgkmcnt left at their maxima).
+    auto wait_loads = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };
+    // The last tile's values past the context end are zeroed in LDS once it
+    // has landed (a weight of 0 does not cancel a NaN); keys there need no
+    // care, their logits are masked by the causal test.
+    auto zero_v_tail = [&](int buf, int t) {
+        const int nval = Lc - t * kKT;            // keys of the tile inside the context
+        if (nval >= kKT) return;
+        __syncthreads();                          // every wave's share of the tile is in LDS
+        for (int e = tid; e < kD * kKT; e += kThreads) {
+            const int d = e / kKT, k = e % kKT;
+            if (k >= nval) sV[buf][d * kKT + 8 * ((k >> 3) ^ ((d >> 1) & 7)) + (k & 7)] = 0;
+        }
+    };
 
     // ---- prologue: ids of tiles 0 and 1, then tile 0 into LDS ----
     if (tid < n_ids) {
-        s_ids[0][tid] = block_id(0, tid);
-        if (nkt > 1) s_ids[1][tid] = block_id(1, tid);
+        s_off[0][tid] = block_id(0, tid) * tile_bytes;
+        if (nkt > 1) s_off[1][tid] = block_id(1, tid) * tile_bytes;
     }
     __syncthreads();
-    load_tile(0, s_ids[0]);
-    store_tile(0);
+    load_tile(0, s_off[0], 0);
+    wait_loads();
+    if (nkt == 1) zero_v_tail(0, 0);
     __syncthreads();
 
     for (int kt = 0; kt < nkt; ++kt) {
         const int buf = kt & 1;
         const int base = kt * kKT;
-        if (kt + 1 < nkt) load_tile(kt + 1, s_ids[buf ^ 1]);
+        if (kt + 1 < nkt) load_tile(kt + 1, s_off[buf ^ 1], buf ^ 1);
         // tile kt + 2's block ids: loaded now, checked and stored after this
         // tile's math, so the wait for them is not on the critical path
         // Every thread loads and checks one id in every iteration (lanes
@@ -308,10 +337,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             f32x16_t s4;
 #pragma unroll
             for (int e = 0; e < 16; ++e) s4[e] = 0.f;
-            const uint16_t* krow = &sK[buf][(32 * t + krow0) * kKStride + 8 * hh];
+            const uint16_t* krow = &sK[buf][(32 * t + krow0) * kD];
 #pragma unroll
             for (int ks = 0; ks < kKS; ++ks) {
-                const u32x4 kf = *reinterpret_cast<const u32x4*>(krow + 16 * ks);
+                const u32x4 kf = *reinterpret_cast<const u32x4*>(krow + 8 * ((2 * ks + hh) ^ kx));
                 s4 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[ks]), s4, 0, 0, 0);
             }
             st[t] = s4;
@@ -332,7 +361,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int e = 0; e < 16; ++e) mx = fmaxf(mx, st[t][e]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = fmaxf(mx, other_half(mx));
         const bool grow = mx > m_run + lazy;
         if (__builtin_amdgcn_ballot_w64(grow)) {
             const float m_new = grow ? mx : m_run;
@@ -350,31 +379,37 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         for (int t = 0; t < 2; ++t) {
             bf16x8_t pb[2];
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(st[t][e], cscale, neg_m));
-                l_run += p;
-                pb[e >> 3][e & 7] = static_cast<__bf16>(p);
+            for (int e = 0; e < 16; ++e)
+                pb[e >> 3][e & 7] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(st[t][e], cscale, neg_m)));
+            // the row sum takes the same bf16 weights as the value product,
+            // two per instruction
+#pragma unroll
+            for (int e = 0; e < 16; e += 2) {
+                const bf16x2_t w2 = {pb[e >> 3][e & 7], pb[e >> 3][(e & 7) + 1]};
+                l_run = __builtin_amdgcn_fdot2_f32_bf16(w2, kOnes2, l_run, false);
             }
             // ---- values: O^T[channel][row] += V^T[channel][key] . P^T[key][row] ----
 #pragma unroll
             for (int mt = 0; mt < kMT; ++mt) {
-                const uint16_t* vrow = &sV[buf][(32 * mt + col) * kVStride + 8 * hh + 32 * t];
+                const uint16_t* vrow = &sV[buf][(32 * mt + col) * kKT];
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
-                    const u32x4 vf = *reinterpret_cast<const u32x4*>(vrow + 16 * kb);
+                    const int sgl = hh + 4 * t + 2 * kb;           // keys base + 8 sgl .. +7
+                    const u32x4 vf = *reinterpret_cast<const u32x4*>(vrow + 8 * (sgl ^ vx));
                     acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), pb[kb], acc[mt], 0, 0, 0);
                 }
             }
         }
-        if (kt + 1 < nkt) store_tile(buf ^ 1);
         const int id = checked(nb_idx, nid);
-        if (next_ids && tid < n_ids) s_ids[buf][tid] = id;
+        if (next_ids && tid < n_ids) s_off[buf][tid] = id * tile_bytes;
+        wait_loads();                             // this wave's share of tile kt + 1 is in LDS
+        if (kt + 2 == nkt) zero_v_tail(buf ^ 1, kt + 1);
         __syncthreads();
     }
     bad = __syncthreads_or(bad);
 
     // ---- normalise and store: lane holds channels 32 mt + 8 (e / 4) + 4 hh + e % 4 of its row ----
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = l_run + other_half(l_run);
     if (!rowok) return;
     const int64_t orow = (static_cast<int64_t>(qs0 + qi) * a.Hq + g * G + (rho & (G - 1))) * kD;
     const float inv = 1.f / l_tot;
