@@ -361,6 +361,7 @@ int pa_decode_append_partitions(void* out, int32_t out_dtype, const void* q, con
  *   q:                device [num_query_tokens][num_q_heads][head_dim] (cache dtype),
  *                     the queries of all chunks back to back; chunk c owns rows
  *                     query_start_loc[c] .. query_start_loc[c+1]-1.
+ *   q, k_cache, v_cache: 16-byte aligned (PA_ERR_INVALID_ARG otherwise).
  *   query_start_loc:  device int32 [num_chunks+1], non-decreasing, within
  *                     [0, num_query_tokens].
  *   context_lens:     device int32 [num_chunks]; L_c counts the chunk's own tokens,
@@ -376,7 +377,8 @@ int pa_decode_append_partitions(void* out, int32_t out_dtype, const void* q, con
  * outside [0, num_blocks) are set to NaN (when they lie inside the output), and
  * nothing is read out of bounds.  Supported: bf16 cache, head_dim 128,
  * num_q_heads/num_kv_heads a power of two up to 16, block_size 8..256 a power
- * of two.  The value pass takes the softmax weights in bf16 (fp32 accumulate). */
+ * of two.  The value pass takes the softmax weights in bf16 (fp32 accumulate),
+ * and each row's weight sum is taken from the same bf16 weights. */
 int pa_prefill(void* out, int32_t out_dtype, const void* q, const void* k_cache,
                const void* v_cache, const pa_cache_desc* desc, const int32_t* block_tables,
                int32_t max_blocks_per_seq, const int32_t* context_lens,

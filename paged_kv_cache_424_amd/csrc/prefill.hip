@@ -454,6 +454,10 @@ extern "C" int pa_prefill(void* out, int32_t out_dtype, const void* q, const voi
     if (num_chunks == 0 || max_query_len == 0 || num_query_tokens == 0) return PA_OK;
     if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start_loc)
         return PA_ERR_INVALID_ARG;
+    // 16-byte loads of q and of the pools
+    if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) |
+         reinterpret_cast<uintptr_t>(v_cache)) % 16)
+        return PA_ERR_INVALID_ARG;
     int log2G = 0;
     while ((1 << log2G) < G) ++log2G;
     const int QT = kRows / G;

@@ -269,6 +269,23 @@ def test_device_calls_reject_bad_host_arguments():
                None) == pa.PA_ERR_UNSUPPORTED
     assert app(one, 0, one, None, None, None, one, one, ref(desc), one, 4, one, 0, 8, 64, 0.1, 0, None, 0,
                None) == pa.PA_OK                     # an empty batch needs nothing
+    # prefill: bf16 cache, head_dim 128, power-of-two groups up to 16 and block sizes 8..256 only;
+    # an empty call needs nothing; q and the pools 16-byte aligned
+    pre = lib.pa_prefill
+    d128 = pa.cache_desc(8, 16, 2, 128, "bf16")
+    d64 = pa.cache_desc(8, 16, 2, 64, "bf16")
+    f32 = pa.cache_desc(8, 16, 2, 128, "f32")
+    big = pa.cache_desc(8, 512, 2, 128, "bf16")
+    assert pre(one, 0, one, one, one, ref(d64), one, 4, one, one, 1, 8, 4, 8, 0.1, None) == pa.PA_ERR_UNSUPPORTED
+    assert pre(one, 0, one, one, one, ref(f32), one, 4, one, one, 1, 8, 4, 8, 0.1, None) == pa.PA_ERR_UNSUPPORTED
+    assert pre(one, 0, one, one, one, ref(big), one, 4, one, one, 1, 8, 4, 8, 0.1, None) == pa.PA_ERR_UNSUPPORTED
+    assert pre(one, 0, one, one, one, ref(d128), one, 4, one, one, 1, 8, 6, 8, 0.1, None) == pa.PA_ERR_UNSUPPORTED
+    assert pre(one, 0, one, one, one, ref(d128), one, 4, one, one, 1, 8, 3, 8, 0.1, None) == pa.PA_ERR_INVALID_ARG
+    assert pre(one, 0, one, one, one, ref(d128), one, 4, one, one, 0, 0, 4, 0, 0.1, None) == pa.PA_OK
+    for i in range(3):
+        ptrs = [one, one, one]
+        ptrs[i] = ctypes.c_void_p(24)
+        assert pre(one, 0, *ptrs, ref(d128), one, 4, one, one, 1, 8, 4, 8, 0.1, None) == pa.PA_ERR_INVALID_ARG
     # 16-byte loads: q and the pools must be 16-byte aligned; k_new and v_new aligned to their element
     odd8 = ctypes.c_void_p(24)
     for i in range(3):

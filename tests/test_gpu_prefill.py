@@ -69,7 +69,8 @@ def test_prefill_last_query_close_to_decode(c5s):
 
 @pytest.mark.parametrize("G,bs,chunk,ctx", [(8, 32, 77, (77, 600)), (4, 16, 300, (300, 1200)),
                                             (1, 16, 40, (40, 200)), (16, 64, 33, (33, 2100)),
-                                            (2, 8, 5, (5, 50))])
+                                            (2, 8, 5, (5, 50)), (4, 128, 100, (100, 900)),
+                                            (2, 256, 70, (300, 1500))])
 def test_prefill_shapes(G, bs, chunk, ctx):
     _announce(f"prefill G={G} bs={bs} chunk={chunk}")
     rng = np.random.default_rng(G * 100 + bs)
