@@ -331,20 +331,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int nid = raw_block_id(nb_idx);
 
         // ---- logits S^T[key][row] for the tile's two 32-key MFMA tiles ----
+        // The two 32-key MFMA chains are interleaved (channel step outer), so
+        // each K fragment read has two MFMAs of lead time and the two
+        // accumulators alternate.
         f32x16_t st[2];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            f32x16_t s4;
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) s4[e] = 0.f;
-            const uint16_t* krow = &sK[buf][(32 * t + krow0) * kD];
+            for (int e = 0; e < 16; ++e) st[t][e] = 0.f;
 #pragma unroll
-            for (int ks = 0; ks < kKS; ++ks) {
+        for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const uint16_t* krow = &sK[buf][(32 * t + krow0) * kD];
                 const u32x4 kf = *reinterpret_cast<const u32x4*>(krow + 8 * ((2 * ks + hh) ^ kx));
-                s4 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[ks]), s4, 0, 0, 0);
+                st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[ks]), st[t], 0, 0, 0);
             }
-            st[t] = s4;
+        // Scheduling hint (LDS reads = 0x100, MFMA = 0x008): 4 fragment reads,
+        // then (2 MFMAs, 2 reads) x 6, then 4 MFMAs, so each read leads its MFMA
+        // by two MFMA pairs instead of one.
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         // element e of tile t holds key base + 32 t + 16 (e / 8) + 8 hh + e % 8
         if (base + kKT - 1 > wave_min_pos) {
 #pragma unroll
