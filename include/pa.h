@@ -51,7 +51,7 @@ typedef enum pa_status {
     PA_ERR_BAD_BLOCK = -3,     /* block id out of range or not allocated */
     PA_ERR_BAD_SEQ = -4,       /* unknown sequence id */
     PA_ERR_HIP = -5,           /* a HIP runtime call or kernel launch failed */
-    PA_ERR_UNSUPPORTED = -6,   /* valid, but a shape this build has no kernel for */
+    PA_ERR_UNSUPPORTED = -6,   /* valid, but a shape the library has no kernel for */
     PA_ERR_NO_MEMORY = -7      /* host allocation failed */
 } pa_status;
 

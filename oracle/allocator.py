@@ -16,7 +16,7 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).  Written from:
       (Copy-on-Write)": requests with the same prefix point at the same physical
       blocks; a request that starts writing something different gets its own copy.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
   * free list order: FIFO.  The pool starts with a given order (default
     0..N-1); allocate takes the head, a block whose reference count falls to
     zero goes to the tail.  Sequence frees release blocks in logical order.
@@ -237,7 +237,7 @@ class PrefixCachingAllocator(BlockAllocator):
     subject: finding reusable prompt blocks automatically); [studynote 223]
     section II copy-on-write paragraph (identical prefixes point at the same
     physical blocks).  The pages give the idea, not the rules; the rules taken
-    here (each listed in the design doc):
+    here:
 
       * A full block's content is identified by (content of the block before
         it, its block_size token ids); the first block's predecessor is the

@@ -18,7 +18,7 @@ gathered context, and that is what is written here:
   3. weights w = exp(z - max z) / sum exp(z - max z);
   4. out = sum_p w_p v_p.
 
-The pages never write the formula; the readings taken (listed in the design doc):
+The pages never write the formula; the readings taken:
 softmax(q K^T * scale) V with scale given by the caller (1/sqrt(D) in every
 workload); query head h reads kv head h // G with G = Hq / Hkv (grouped-query
 attention); a decode context length L includes the newly written token; a

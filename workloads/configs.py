@@ -1,6 +1,6 @@
 """The five workloads, as seeded synthetic inputs.
 
-Recipe (also stated in the design doc): numpy ``default_rng(seed)`` (PCG64), seed =
+Recipe: numpy ``default_rng(seed)`` (PCG64), seed =
 the workload's number 1..5 unless overridden; values N(0,1) drawn as float32;
 bf16 caches and queries are the float32 draws rounded to nearest-even by torch
 on the CPU.  Draw order: lengths, then the pool's initial free-block
