@@ -83,10 +83,10 @@ def test_full_decode_sampled(full):
         assert err <= BUDGET, (part, err)
 
 
+@pytest.mark.parametrize("full", ["c5"], indirect=True)      # the workload with prefill chunks
 def test_full_prefill_sampled(full):
     name, w, st_o, st_l = full
-    if not w.prefill_seqs:
-        pytest.skip("no prefill chunks in this workload")
+    assert w.prefill_seqs
     _announce(f"prefill {name} (full size)")
     qs = np.concatenate([[0], np.cumsum(w.chunk_len)])
     rng = np.random.default_rng(1)
