@@ -126,6 +126,7 @@ _DEC = [_vp, _i32, _vp, _vp, _vp, _PD, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _
 _sig("pa_decode", ctypes.c_int, *_DEC)
 _sig("pa_decode_partitions", ctypes.c_int, *_DEC)
 _sig("pa_decode_reduce", ctypes.c_int, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp)
+_sig("pa_time_next_partitions", ctypes.c_int, _vp, _vp)
 _DEC_APPEND = [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _PD, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _i32,
                _vp, _sz, _vp]
 _sig("pa_decode_append", ctypes.c_int, *_DEC_APPEND)
@@ -406,6 +407,21 @@ def pa_decode_append_partitions(out, q, k_new, v_new, slot_mapping, k_cache, v_c
                                                           max_context_len, scale, partition_size,
                                                           workspace, stream)),
            "pa_decode_append_partitions")
+
+
+def pa_time_next_partitions(start, stop):
+    """Have the next partition pass (pa_decode_partitions or
+    pa_decode_append_partitions) of this thread record start / stop
+    (torch.cuda.Event, already recorded once so their HIP events exist) at its
+    kernel's own dispatch start and end."""
+    def handle(ev):
+        if ev is None:
+            return None
+        h = int(ev.cuda_event)
+        if not h:
+            raise ValueError("event has no HIP event yet: record it once first")
+        return ctypes.c_void_p(h)
+    _check(_lib.pa_time_next_partitions(handle(start), handle(stop)), "pa_time_next_partitions")
 
 
 def pa_decode_reduce(out, context_lens, num_q_heads, head_dim, max_context_len, partition_size=0,

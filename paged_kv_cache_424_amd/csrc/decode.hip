@@ -821,8 +821,17 @@ int device_cus(int* cus) {
     return PA_OK;
 }
 
+// Events set by pa_time_next_partitions for the next partition pass of this
+// host thread: start goes with its first kernel launch, stop with its last.
+struct PartitionTiming {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+thread_local PartitionTiming g_time_next;
+
 template <bool BF16, int D>
 int launch_partitions(const DecodeArgs& a0, int32_t num_seqs, const Plan& c, hipStream_t st) {
+    const PartitionTiming timing = g_time_next;
+    g_time_next = PartitionTiming{};
     const bool fixed = c.part_chunks > 0;
     const bool app = a0.k_new != nullptr;
     const auto kernel = fixed ? (app ? decode_partition_kernel<BF16, D, true, true>
@@ -874,7 +883,9 @@ int launch_partitions(const DecodeArgs& a0, int32_t num_seqs, const Plan& c, hip
             const int64_t items = static_cast<int64_t>(nb) * a.H * ((nch + kMinPieceChunks - 1) / kMinPieceChunks);
             grid = std::max<int64_t>(1, std::min<int64_t>(static_cast<int64_t>(per_cu) * cus, items));
         }
-        rc = launch_kernel(kernel, dim3(static_cast<uint32_t>(grid)), dim3(64 * waves), lds, st, a);
+        rc = launch_kernel_timed(kernel, dim3(static_cast<uint32_t>(grid)), dim3(64 * waves), lds, st,
+                                 s0 == 0 ? timing.start : nullptr,
+                                 s0 + kMaxSeqsPerLaunch >= num_seqs ? timing.stop : nullptr, a);
         if (rc != PA_OK) return rc;
     }
     return PA_OK;
@@ -993,6 +1004,12 @@ int pa_decode_append_partitions(void* out, int32_t out_dtype, const void* q, con
                                  max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
                                  max_context_len, scale, partition_size, workspace, workspace_bytes,
                                  stream, k_new, v_new, slot_mapping, k_cache, v_cache);
+}
+
+int pa_time_next_partitions(void* start_event, void* stop_event) {
+    pa::g_time_next.start = static_cast<hipEvent_t>(start_event);
+    pa::g_time_next.stop = static_cast<hipEvent_t>(stop_event);
+    return PA_OK;
 }
 
 int pa_decode_reduce(void* out, int32_t out_dtype, const int32_t* context_lens, int32_t num_seqs,

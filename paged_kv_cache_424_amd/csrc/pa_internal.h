@@ -1,6 +1,7 @@
 // Internal helpers shared by the HIP translation units of the library.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -31,9 +32,12 @@ inline int hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : record_hi
 // own return code is used, never hipGetLastError(): the latter also reports
 // errors left behind by unrelated HIP calls of the host program.  Arguments
 // are converted to the kernel's parameter types first.  Does not synchronize.
+// With start/stop events (either may be null) the launch goes through
+// hipExtLaunchKernel, which records them at the start and the end of the
+// kernel's own dispatch.
 template <typename... KArgs, typename... Args>
-int launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds, hipStream_t st,
-                  Args... args) {
+int launch_kernel_timed(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds, hipStream_t st,
+                        hipEvent_t start, hipEvent_t stop, Args... args) {
     static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count");
     std::tuple<KArgs...> vals(static_cast<KArgs>(args)...);
     void* ptrs[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1] = {};
@@ -43,8 +47,17 @@ int launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds, h
             ((ptrs[i++] = const_cast<void*>(static_cast<const void*>(&v))), ...);
         },
         vals);
+    if (start || stop)
+        return hip_status(hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, lds,
+                                             st, start, stop, 0));
     return hip_status(
         hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, lds, st));
+}
+
+template <typename... KArgs, typename... Args>
+int launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds, hipStream_t st,
+                  Args... args) {
+    return launch_kernel_timed(kernel, grid, block, lds, st, nullptr, nullptr, args...);
 }
 
 constexpr int kNumXcds = 8;   // MI355X: 8 XCDs, workgroups dispatched round-robin over them

@@ -158,3 +158,30 @@ def test_slot_elsewhere_is_stored_not_read(part):
     assert torch.isnan(got[0::2]).all() and not torch.isnan(got[1::2]).any()
     for a, b in ((st.kc, ref_st.kc), (st.vc, ref_st.vc)):
         assert np.array_equal(lib_run.pool_bits(a, w.dtype), lib_run.pool_bits(b, w.dtype))
+
+
+def test_partition_timing_hook_changes_nothing():
+    # pa_time_next_partitions: the next partition pass records the two events
+    # with its kernel's dispatch; results are those of an untimed call
+    _announce("partition timing hook")
+    w = workloads.make("c2", small=True)
+    st = lib_run.build(w)
+    B, Hq, D = st.q.shape
+    wsb = pa.pa_decode_workspace_bytes(B, Hq, D, st.max_ctx, 512)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    outs = []
+    for timed in (False, True):
+        out = torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+        ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        for e in ev:
+            e.record()
+        if timed:
+            pa.pa_time_next_partitions(*ev)
+        pa.pa_decode_partitions(out, st.q, st.kc, st.vc, st.desc, st.tables, st.lens, st.max_ctx, w.scale,
+                                512, ws)
+        pa.pa_decode_reduce(out, st.lens, Hq, D, st.max_ctx, 512, ws)
+        torch.cuda.synchronize()
+        if timed:
+            assert ev[0].elapsed_time(ev[1]) > 0
+        outs.append(out)
+    assert torch.equal(outs[0], outs[1])
