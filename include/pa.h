@@ -355,13 +355,16 @@ int pa_decode_append_partitions(void* out, int32_t out_dtype, const void* q, con
                                 int32_t partition_size, void* workspace, size_t workspace_bytes,
                                 void* stream);
 
-/* Kernel timing: the next pa_decode_partitions or pa_decode_append_partitions
- * call of the calling host thread records start_event when its first
+/* Kernel timing: the next partition pass of the calling host thread (that of
+ * pa_decode, pa_decode_append, pa_decode_partitions or
+ * pa_decode_append_partitions) records start_event when its first
  * partition-kernel dispatch starts and stop_event when its last one ends
  * (hipExtLaunchKernel's dispatch events, the same clock a kernel trace
- * reports); then the request is cleared.  Events are hipEvent_t values the
- * caller created; either may be NULL (NULL and NULL clears a pending request).
- * Nothing else changes: same kernels, same results.  Returns PA_OK. */
+ * reports); the request is then cleared.  A call that returns an error before
+ * launching leaves it pending.  Events are hipEvent_t values the caller
+ * created, on the call's device; either may be NULL (NULL and NULL clears a
+ * pending request).  Same kernels, same results; such a launch costs a few
+ * microseconds more than a plain one.  Returns PA_OK. */
 int pa_time_next_partitions(void* start_event, void* stop_event);
 
 /* Causal attention of prefill chunks over their paged context, the prefill half
