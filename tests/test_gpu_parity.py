@@ -214,6 +214,53 @@ def test_decode_shapes(dtype, D, G, bs):
         assert np.max(np.abs(got - want)) <= BUDGET[dtype], part
 
 
+@pytest.mark.parametrize("seed", range(16))
+def test_decode_random_configs(seed):
+    # seeded random configurations: cache dtype, head size, group size (1..16),
+    # kv heads, block size (8..256), batch size, a length mix with block and
+    # chunk edges, and the partition (balanced, 32-token, or 64..1024 tokens);
+    # the plain decode against the oracle, and decode with append bit-identical
+    # to write + decode
+    import paged_kv_cache_424_amd as pa
+    rng = np.random.default_rng(1000 + seed)
+    dtype = ["bf16", "f32"][seed % 2]
+    D = [64, 128][(seed // 2) % 2]
+    G = int(rng.integers(1, 17))
+    Hkv = int(rng.integers(1, 5))
+    bs = int(2 ** rng.integers(3, 9))
+    B = int(rng.integers(1, 24))
+    edges = [1, 2, bs, bs + 1, 31, 32, 33, 511, 512, 513]
+    lens = [int(x) if rng.random() < 0.6 else int(rng.choice(edges)) for x in rng.integers(1, 1800, size=B)]
+    part = int(rng.choice([0, 32, 64, 160, 512, 1024]))
+    _announce(f"decode random config {seed}: {dtype} D={D} G={G} Hkv={Hkv} bs={bs} B={B} partition {part}")
+    w = workloads.decode_batch(seed=seed, lens=lens, name="rnd", Hq=G * Hkv, Hkv=Hkv, D=D, bs=bs, dtype=dtype)
+    st_o, ref_st = oracle_run.build(w), lib_run.build(w)
+    want = oracle_run.oracle_decode(w, st_o)
+    ref = lib_run.decode(w, ref_st, partition_size=part)
+    got = ref.double().cpu().numpy()
+    assert np.isfinite(got).all()
+    assert np.max(np.abs(got - want)) <= BUDGET[dtype]
+    # decode with append: the step's newest tokens stored by the decode kernel
+    st = lib_run.build(w, run_step=False)
+    slots, rows = [], []
+    for sl, rw in st.step_writes:
+        slots.append(int(sl[0]))
+        rows.append(int(rw[0]))
+    k_new = lib_run.torch_stored(w.k_tok[rows], w.dtype).cuda()
+    v_new = lib_run.torch_stored(w.v_tok[rows], w.dtype).cuda()
+    B_, Hq, _ = st.q.shape
+    out = torch.full((B_, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    wsb = pa.pa_decode_workspace_bytes(B_, Hq, D, st.max_ctx, part)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda") if wsb else None
+    pa.pa_decode_append(out, st.q, k_new, v_new, torch.tensor(slots, dtype=torch.int64, device="cuda"),
+                        st.kc, st.vc, st.desc, st.tables, st.lens, st.max_ctx, w.scale, partition_size=part,
+                        workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    for a, b in ((st.kc, ref_st.kc), (st.vc, ref_st.vc)):
+        assert np.array_equal(lib_run.pool_bits(a, w.dtype), lib_run.pool_bits(b, w.dtype))
+
+
 # ---- probes with sharp structure -------------------------------------------------------
 def _probe_workload(base, k=None, v=None, q=None):
     return dataclasses.replace(base, k_tok=base.k_tok if k is None else k,
