@@ -108,6 +108,50 @@ def test_prefill_shapes(G, bs, chunk, ctx):
     assert np.isfinite(got).all() and err <= TOL, err
 
 
+@pytest.mark.parametrize("seed", range(10))
+def test_prefill_random_configs(seed):
+    # seeded random configurations: group size (a power of two up to 16), kv
+    # heads, block size (8..256), 1-4 chunks of random length (one may have no
+    # earlier context), random contexts; against the oracle
+    rng = np.random.default_rng(2000 + seed)
+    G = int(2 ** rng.integers(0, 5))
+    H = int(rng.integers(1, 5))
+    bs = int(2 ** rng.integers(3, 9))
+    n_chunks = int(rng.integers(1, 5))
+    D = 128
+    Hq = H * G
+    chunks = [int(rng.integers(1, 300)) for _ in range(n_chunks)]
+    clens = [c + (0 if rng.random() < 0.25 else int(rng.integers(0, 1500))) for c in chunks]
+    _announce(f"prefill random config {seed}: G={G} H={H} bs={bs} chunks={chunks} contexts={clens}")
+    need = sum(-(-L // bs) for L in clens)
+    N = need + 3
+    free_order = rng.permutation(N).astype(np.int32)
+    total = sum(clens)
+    k = workloads.configs._normals(rng, (total, H, D), "bf16")
+    v = workloads.configs._normals(rng, (total, H, D), "bf16")
+    q = workloads.configs._normals(rng, (sum(chunks), Hq, D), "bf16")
+    script, rows, r0 = [], {}, 0
+    for s_, L in enumerate(clens):
+        script.append(("setup", ("create",)))
+        rows[s_] = np.arange(r0, r0 + L)
+        r0 += L
+    for s_, L in enumerate(clens):
+        if L > chunks[s_]:
+            script.append(("setup", ("append", s_, L - chunks[s_])))
+    for s_ in range(n_chunks):
+        script.append(("step", ("append", s_, chunks[s_])))
+    w = workloads.Workload(name="pre", dtype="bf16", num_q_heads=Hq, num_kv_heads=H, head_dim=D,
+                           block_size=bs, num_blocks=N, free_order=free_order, scale=D ** -0.5,
+                           script=script, tok_rows=rows, k_tok=k, v_tok=v, decode_seqs=[],
+                           q_dec=np.zeros((0, Hq, D), dtype=np.uint16),
+                           prefill_seqs=list(range(n_chunks)), chunk_len=chunks, q_pre=q)
+    st_o, st_l = oracle_run.build(w), lib_run.build(w)
+    want = oracle_run.oracle_prefill(w, st_o)
+    got = lib_run.prefill(w, st_l).double().cpu().numpy()
+    err = np.max(np.abs(got - want))
+    assert np.isfinite(got).all() and err <= TOL, err
+
+
 def test_prefill_needle_and_causality(c5s):
     # a key placed after a query must not influence it: put a huge needle at
     # each chunk's last position; only the chunk's last query may see it
