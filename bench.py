@@ -14,7 +14,7 @@ resident in HBM:
 Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload c2|c3|c4|c4p|c5]
-    python bench.py --study prefix-cache|fragmentation|block-size|batch1
+    python bench.py --study prefix-cache|fragmentation|block-size|batch1|stream-peak
 
 Default workload (c2): Llama-3-8B-shaped decode.
 - 64 sequences, context lengths U{128..2048}.
@@ -56,6 +56,9 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak, GB/s
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA peak, TFLOP/s
 METRIC = "paged decode attention: seq-tokens/s and achieved HBM GB/s (% of peak)"
 CALIB_BYTES = 1 << 30          # size of the plain copy that calibrates the byte counters
+# streaming-read launch shapes timed beside the decode, (workgroups per CU,
+# loads per thread, blocked order): the fastest of the stream-peak study
+STREAM_SHAPES_BENCH = ((32, 1, 0), (8, 8, 1), (16, 8, 1), (32, 4, 1))
 
 WORKLOAD_TEXT = {
     "c2": "Llama-3-8B-shaped decode: 64 sequences, context U{128..2048}, 32/8 heads, head_dim 128, "
@@ -217,7 +220,7 @@ def main():
     ap.add_argument("--fetch-dir")
     ap.add_argument("--write-dir")
     ap.add_argument("--command", help="the profiled command, recorded in the summary")
-    ap.add_argument("--study", choices=["prefix-cache", "fragmentation", "block-size", "batch1"],
+    ap.add_argument("--study", choices=["prefix-cache", "fragmentation", "block-size", "batch1", "stream-peak"],
                     help="run one of the studies in bench_studies.py instead of the benchmark")
     args = ap.parse_args()
     if args.pmc_summary:
@@ -439,6 +442,17 @@ def main():
                        "decode_partitions": avg_us(2, 3), "decode_reduce": avg_us(3, 4),
                        "prefill": avg_us(4, 5) if pre is not None else None},
     }
+    # the practical read rate for the same byte count: a plain streaming read
+    # of one contiguous buffer (pa_stream_read), best of a few launch shapes,
+    # measured after everything above
+    import bench_studies
+    sbytes, _, srates = bench_studies.stream_read_rates(algo, 10, shapes=STREAM_SHAPES_BENCH)
+    sbest = max(srates, key=lambda k: srates[k]["gbs"])
+    res["roofline"]["stream_read_same_bytes"] = {
+        "gbs": srates[sbest]["gbs"], "frac_of_peak": srates[sbest]["gbs"] / PEAK_HBM_GBS,
+        "bytes": sbytes, "launch_shape": sbest,
+        "decode_over_stream": achieved / srates[sbest]["gbs"],
+        "kernel": "stream_read_kernel: one contiguous buffer, 16-byte non-temporal loads"}
     if pre is not None:
         pre_ms = [e[4].elapsed_time(e[5]) for e in evs]
         pre_s = float(np.mean(pre_ms)) / 1e3

@@ -5,6 +5,7 @@ on the library (C ABI through the binding).  Run through bench.py:
     python bench.py --study fragmentation   # host only
     python bench.py --study block-size      # GPU
     python bench.py --study batch1          # GPU
+    python bench.py --study stream-peak     # GPU
 
 Each prints one JSON line per configuration it measures.
 
@@ -30,6 +31,10 @@ block-size: the Llama-3-8B-shaped decode batch stored with 8, 16, 32, 64 and
     against the slots left empty in last blocks and the size of the block
     tables.  [studynote 223]
     section IV, checklist item 1; [ch.09] "한계와 트레이드오프".
+stream-peak: a plain streaming read (pa_stream_read: one contiguous buffer,
+    16-byte non-temporal loads, grid-stride) of the decode workloads' byte
+    counts and of 4 GiB, over a few launch shapes: the practical HBM read rate
+    beside the 8 TB/s spec.
 batch1: one sequence of 512..32768 tokens, its blocks scattered over the pool
     or laid out in order (identity table), beside 64 sequences of the same
     length: what the indirection and a single sequence cost.  [studynote 223]
@@ -405,5 +410,52 @@ def study_batch1(args):
                 torch.cuda.empty_cache()
 
 
+# launch shapes of the streaming read: (workgroups per CU, loads in flight per
+# thread, blocked order)
+STREAM_SHAPES = ((4, 4, 0), (16, 8, 0), (32, 1, 0), (64, 1, 0), (4, 8, 1), (4, 16, 1), (8, 4, 1),
+                 (8, 8, 1), (8, 16, 1), (16, 4, 1), (16, 8, 1), (32, 4, 1))
+
+
+def stream_read_rates(nbytes, reps, shapes=STREAM_SHAPES):
+    """GB/s of pa_stream_read over nbytes for each launch shape (HIP events
+    around each launch; consecutive launches read buffers at least 1 GiB apart
+    in total, so no launch is served from the Infinity Cache)."""
+    import torch
+    import paged_kv_cache_424_amd as pa
+    nbytes = max(16, nbytes // 16 * 16)
+    copies = 1 if nbytes >= ROTATE_BYTES else -(-ROTATE_BYTES // nbytes) + 1
+    bufs = [torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda") for _ in range(copies)]
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    rates = {}
+    for bpc, unroll, blocked in shapes:
+        for i in range(3):
+            pa.pa_stream_read(bufs[i % copies], sink, bpc, unroll, blocked)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for i, (e0, e1) in enumerate(evs):
+            e0.record()
+            pa.pa_stream_read(bufs[(3 + i) % copies], sink, bpc, unroll, blocked)
+            e1.record()
+        torch.cuda.synchronize()
+        us = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) * 1e3
+        rates[f"{bpc}x{unroll}{'b' if blocked else 's'}"] = {"us": us, "gbs": nbytes / (us * 1e-6) / 1e9}
+    del bufs
+    torch.cuda.empty_cache()
+    return nbytes, copies, rates
+
+
+def study_stream_peak(args):
+    import torch
+    torch.cuda.set_device(0)
+    # the decode workloads' algorithmic bytes per launch, and a large read
+    sizes = {"c2 decode bytes": 302_668_092, "c3 decode bytes": 1_074_004_992, "4 GiB": 4 << 30}
+    for name, n in sizes.items():
+        nbytes, copies, rates = stream_read_rates(n, args.steps)
+        best = max(rates, key=lambda k: rates[k]["gbs"])
+        _emit({"study": "stream_peak", "size": name, "bytes": nbytes, "buffers": copies,
+               "launches": args.steps, "best_shape": best, "best_gbs": rates[best]["gbs"],
+               "best_frac_of_8tbs": rates[best]["gbs"] / 8000.0,
+               "shapes": {k: round(v["gbs"], 1) for k, v in rates.items()}})
+
+
 STUDIES = {"prefix-cache": study_prefix_cache, "fragmentation": study_fragmentation,
-           "block-size": study_block_size, "batch1": study_batch1}
+           "block-size": study_block_size, "batch1": study_batch1, "stream-peak": study_stream_peak}

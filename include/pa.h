@@ -397,6 +397,27 @@ int pa_prefill(void* out, int32_t out_dtype, const void* q, const void* k_cache,
                const int32_t* query_start_loc, int32_t num_chunks, int32_t num_query_tokens,
                int32_t num_q_heads, int32_t max_query_len, float scale, void* stream);
 
+/* ---- measurement ------------------------------------------------------------------ */
+
+/* A plain streaming read of one contiguous device buffer: the practical HBM
+ * read rate of this device, the yardstick beside the spec peak for
+ * pa_decode's rate (pa_decode reads the same kind of bytes, scattered over
+ * blocks).  Not part of the attention path.
+ *   src:           device, 16-byte aligned; bytes a multiple of 16.
+ *   blocks_per_cu: workgroups (256 threads) per compute unit, 1..64; the
+ *                  grid-stride loop covers any size.
+ *   unroll:        independent 16-byte non-temporal loads per thread and loop
+ *                  trip: 1, 4, 8 or 16 (PA_ERR_UNSUPPORTED otherwise).
+ *   blocked:       0: grid-stride (each load of the grid covers one contiguous
+ *                  band, 4 KB per workgroup); 1: each workgroup reads
+ *                  unroll x 4 KB contiguous bytes per loop trip.
+ *   sink:          device, 4 bytes, written only in the unlikely case that the
+ *                  XOR of all words a thread read equals 0x9e3779b9.
+ * PA_ERR_INVALID_ARG for a null pointer, misalignment, blocks_per_cu outside
+ * 1..64 or blocked not 0 or 1.  Asynchronous on stream. */
+int pa_stream_read(const void* src, size_t bytes, int32_t blocks_per_cu, int32_t unroll, int32_t blocked,
+                   void* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -133,6 +133,7 @@ _sig("pa_decode_append", ctypes.c_int, *_DEC_APPEND)
 _sig("pa_decode_append_partitions", ctypes.c_int, *_DEC_APPEND)
 _sig("pa_prefill", ctypes.c_int, _vp, _i32, _vp, _vp, _vp, _PD, _vp, _i32, _vp, _vp, _i32, _i32,
      _i32, _i32, _f32, _vp)
+_sig("pa_stream_read", ctypes.c_int, _vp, _sz, _i32, _i32, _i32, _vp, _vp)
 
 
 def _check(rc, where):
@@ -442,3 +443,12 @@ def pa_prefill(out, q, k_cache, v_cache, desc, block_tables, context_lens, query
                            int(q.shape[0]), int(q.shape[1]), int(max_query_len), float(scale),
                            _stream(stream)),
            "pa_prefill")
+
+
+def pa_stream_read(src, sink, blocks_per_cu=8, unroll=4, blocked=0, stream=None):
+    """Plain streaming read of the whole device tensor src (a measurement
+    yardstick, not part of the attention path); sink: a device tensor of at
+    least 4 bytes."""
+    _check(_lib.pa_stream_read(_dev(src, "src"), src.numel() * src.element_size(), int(blocks_per_cu),
+                               int(unroll), int(blocked), _dev(sink, "sink"), _stream(stream)),
+           "pa_stream_read")

@@ -417,3 +417,19 @@ def test_prompt_cache_workload_script_bit_exact(small):
         assert st["evictions"] > 0 and st["hit_tokens"] == hits
     finally:
         pa.pa_allocator_destroy(h)
+
+
+def test_stream_read_rejects_bad_host_arguments():
+    # the streaming-read yardstick checks its arguments before any HIP call
+    lib = _lib()
+    one = ctypes.c_void_p(16)
+    sr = lib.pa_stream_read
+    assert sr(None, 64, 8, 4, 0, one, None) == pa.PA_ERR_INVALID_ARG
+    assert sr(one, 64, 8, 4, 0, None, None) == pa.PA_ERR_INVALID_ARG
+    assert sr(ctypes.c_void_p(24), 64, 8, 4, 0, one, None) == pa.PA_ERR_INVALID_ARG   # src not 16-byte aligned
+    assert sr(one, 40, 8, 4, 0, one, None) == pa.PA_ERR_INVALID_ARG                    # not a multiple of 16
+    assert sr(one, 64, 0, 4, 0, one, None) == pa.PA_ERR_INVALID_ARG
+    assert sr(one, 64, 65, 4, 0, one, None) == pa.PA_ERR_INVALID_ARG
+    assert sr(one, 64, 8, 4, 2, one, None) == pa.PA_ERR_INVALID_ARG
+    assert sr(one, 64, 8, 3, 0, one, None) == pa.PA_ERR_UNSUPPORTED
+    assert sr(one, 0, 8, 4, 1, one, None) == pa.PA_OK                                  # nothing to read
