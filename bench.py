@@ -9,7 +9,9 @@ resident in HBM:
    decode sequence's newest token, the decode kernel stores them itself
    instead (pa_decode_append; --append on/off overrides);
 3. the split-K decode partition kernel, then the rescaling reduce;
-4. for the mixed continuous-batching workload, the prefill-chunk kernel.
+4. for the mixed continuous-batching workload, the prefill-chunk kernel, after
+   the decode (--overlap on runs it on a second stream beside the decode;
+   both wait for the cache write).
 
 Prints one JSON line.
 
@@ -209,6 +211,10 @@ def main():
                     help="store each decode sequence's newest token inside the decode kernel "
                          "(pa_decode_append) instead of a separate cache write; auto: when the "
                          "step writes no other token (a cache-write launch happens anyway otherwise)")
+    ap.add_argument("--overlap", choices=["on", "off"], default="off",
+                    help="run the prefill chunks on a second stream, concurrently with the decode "
+                         "(both wait for the step's cache write); the per-kernel figures are then "
+                         "taken while the two kernels share the chip")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the extra HIP-graph replay measurement of the whole step")
@@ -309,14 +315,23 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # The mixed step's prefill chunks read the pools the cache write has just
+    # filled and nothing the decode writes, so they can run on a second stream
+    # (default priority) beside the decode: the decode streams HBM while the
+    # prefill keeps the matrix cores busy.  The main stream waits for the
+    # second at the end of the step.
+    overlap = pre is not None and args.overlap == "on"
+    side = torch.cuda.Stream() if overlap else None
+
     # Events: in the timed steps only around the partition kernel (2, 3) and
-    # the prefill kernel (4, 5), so that event records add no gaps elsewhere;
+    # the prefill kernel (5, 6), so that event records add no gaps elsewhere;
     # a separate pass after the timed region records all of them: 0 start,
     # 1 after copy_blocks, 2 after cache_write, 3 after the partition kernel,
-    # 4 after the reduce, 5 after prefill.
-    timed_marks = (2, 3, 4, 5) if pre is not None else (2, 3)
+    # 4 after the reduce, 5 before and 6 after prefill (on the prefill's stream).
+    timed_marks = (2, 3, 5, 6) if pre is not None else (2, 3)
 
-    def step(i, ev=None, marks=timed_marks, dispatch_ev=None):
+    def step(i, ev=None, marks=timed_marks, dispatch_ev=None, use_side=None):
+        use_side = overlap if use_side is None else use_side
         def mark(k):
             if ev is not None and k in marks:
                 ev[k].record()
@@ -328,6 +343,27 @@ def main():
         if slots.numel():
             pa.pa_cache_write(kc, vc, st.desc, k_new, v_new, slots)
         mark(2)
+
+        def prefill():
+            mark(5)
+            pa.pa_prefill(pre["out"], pre["q"], kc, vc, st.desc, pre["tables"], pre["lens"], pre["qsl"],
+                          pre["max_q"], w.scale)
+            mark(6)
+        joined = None
+        main = torch.cuda.current_stream()
+        if pre is not None and use_side:
+            side.wait_stream(main)                              # after the cache write
+            with torch.cuda.stream(side):
+                prefill()
+                joined = torch.cuda.Event()
+                joined.record()
+        decode(kc, vc, mark, dispatch_ev)
+        if pre is not None and not use_side:
+            prefill()
+        if joined is not None:
+            main.wait_event(joined)
+
+    def decode(kc, vc, mark, dispatch_ev):
         if dispatch_ev is not None:
             pa.pa_time_next_partitions(*dispatch_ev)
         if newest is not None:
@@ -339,15 +375,11 @@ def main():
         mark(3)
         pa.pa_decode_reduce(out, st.lens, Hq, D, max_ctx, args.partition, ws)
         mark(4)
-        if pre is not None:
-            pa.pa_prefill(pre["out"], pre["q"], kc, vc, st.desc, pre["tables"], pre["lens"], pre["qsl"],
-                          pre["max_q"], w.scale)
-        mark(5)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(6)) for _ in range(args.steps)]
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(7)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -372,10 +404,20 @@ def main():
 
     ms_per_step = wall * 1e3 / args.steps
 
+    # the same steps with the prefill on the decode's stream, for comparison
+    serial_ms = None
+    if overlap:
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for i in range(args.steps):
+            step(args.warmup + i, use_side=False)
+        torch.cuda.synchronize()
+        serial_ms = (time.perf_counter() - t1) * 1e3 / args.steps
+
     # per-kernel times, all events recorded (not part of the timed region)
-    evk = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(6)) for _ in range(args.steps)]
+    evk = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(7)) for _ in range(args.steps)]
     for i in range(args.steps):
-        step(args.warmup + i, evk[i], marks=(0, 1, 2, 3, 4, 5))
+        step(args.warmup + i, evk[i], marks=(0, 1, 2, 3, 4, 5, 6), use_side=False)
     torch.cuda.synchronize()
 
     def avg_us(a, b):
@@ -426,21 +468,25 @@ def main():
                    "step": ("copy_blocks + " if pairs else "") +
                            ("cache_write + " if slots.numel() else "") +
                            ("decode_append_partitions" if newest is not None else "decode_partitions") +
-                           " + decode_reduce" + (" + prefill" if pre is not None else "")},
+                           " + decode_reduce" + ((" || prefill (second stream)" if overlap else " + prefill")
+                                                 if pre is not None else "")},
         "roofline": {"bound": "hbm", "kernel": "decode_partition_kernel", "achieved": achieved,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                      "traffic": load_traffic(args.workload), "algorithmic_bytes_per_launch": algo,
                      "avg_launch_us": part_avg_s * 1e6, "p10_us": float(np.percentile(part_ms, 10)) * 1e3,
                      "p90_us": float(np.percentile(part_ms, 90)) * 1e3,
-                     "timing": "HIP events recorded around the launch call in the timed steps",
+                     "timing": "HIP events recorded around the launch call in the timed steps" +
+                               (", while the prefill runs on a second stream" if overlap else ""),
                      "avg_launch_us_dispatch_events": float(np.mean(dispatch_ms)) * 1e3,
                      "kernel_source_hash": kernel_source_hash()},
         "decode_gbs_whole_step": algo / (ms_per_step / 1e3) / 1e9,
         "hip_graph_ms_per_step": graph_ms,
+        "prefill_on_second_stream": overlap,
+        "ms_per_step_one_stream": serial_ms,
         "kernels_us_untimed_pass": {"copy_blocks": avg_us(0, 1) if pairs else None,
                                     "cache_write": avg_us(1, 2) if slots.numel() else None,
                        "decode_partitions": avg_us(2, 3), "decode_reduce": avg_us(3, 4),
-                       "prefill": avg_us(4, 5) if pre is not None else None},
+                       "prefill": avg_us(5, 6) if pre is not None else None},
     }
     # the practical read rate for the same byte count: a plain streaming read
     # of one contiguous buffer (pa_stream_read), best of a few launch shapes,
@@ -454,14 +500,15 @@ def main():
         "decode_over_stream": achieved / srates[sbest]["gbs"],
         "kernel": "stream_read_kernel: one contiguous buffer, 16-byte non-temporal loads"}
     if pre is not None:
-        pre_ms = [e[4].elapsed_time(e[5]) for e in evs]
+        pre_ms = [e[5].elapsed_time(e[6]) for e in evs]
         pre_s = float(np.mean(pre_ms)) / 1e3
         tf = pre["flops"] / pre_s / 1e12
         assert torch.isfinite(pre["out"]).all()
         res["prefill"] = {"bound": "mfma", "kernel": "prefill_kernel", "achieved": tf,
                           "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
                           "flops_per_launch": pre["flops"], "avg_launch_us": pre_s * 1e6,
-                          "timing": "HIP events recorded around the launch call",
+                          "timing": "HIP events recorded around the launch call" +
+                                    (" on the second stream, while the decode runs" if overlap else ""),
                           "query_tokens": int(sum(w.chunk_len))}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
