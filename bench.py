@@ -201,8 +201,8 @@ def prefill_flops(w, clens):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c2", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--partition", type=int, default=512,
                     help="split-K partition in tokens (a multiple of 32), or 0 for the balanced split; "
@@ -473,7 +473,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "decode_partition_kernel", "achieved": achieved,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                      "traffic": load_traffic(args.workload), "algorithmic_bytes_per_launch": algo,
-                     "avg_launch_us": part_avg_s * 1e6, "p10_us": float(np.percentile(part_ms, 10)) * 1e3,
+                     "avg_launch_us": part_avg_s * 1e6, "median_us": float(np.median(part_ms)) * 1e3,
+                     "p10_us": float(np.percentile(part_ms, 10)) * 1e3,
                      "p90_us": float(np.percentile(part_ms, 90)) * 1e3,
                      "timing": "HIP events recorded around the launch call in the timed steps" +
                                (", while the prefill runs on a second stream" if overlap else ""),
@@ -507,6 +508,9 @@ def main():
         res["prefill"] = {"bound": "mfma", "kernel": "prefill_kernel", "achieved": tf,
                           "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
                           "flops_per_launch": pre["flops"], "avg_launch_us": pre_s * 1e6,
+                          "median_us": float(np.median(pre_ms)) * 1e3,
+                          "p10_us": float(np.percentile(pre_ms, 10)) * 1e3,
+                          "p90_us": float(np.percentile(pre_ms, 90)) * 1e3,
                           "timing": "HIP events recorded around the launch call" +
                                     (" on the second stream, while the decode runs" if overlap else ""),
                           "query_tokens": int(sum(w.chunk_len))}
