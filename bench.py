@@ -18,12 +18,18 @@ Prints one JSON line.
     python bench.py [--steps K] [--warmup W] [--workload c2|c3|c4|c4p|c5]
     python bench.py --study prefix-cache|fragmentation|block-size|batch1|stream-peak
 
-Default workload (c2): Llama-3-8B-shaped decode.
-- 64 sequences, context lengths U{128..2048}.
-- 32 query / 8 KV heads, head_dim 128.
-- bf16 cache in 16-token blocks, pool = blocks needed + 10 %.
-- One new token per sequence is written, then decoded in 512-token
-  partitions (--partition; 0 selects the balanced split).
+Default workload (c5): the mixed continuous-batching step at 70B-shaped heads,
+the largest configuration that fits one GPU.
+- 240 decode sequences, lognormal context lengths (median 1024, [64, 8192]),
+  plus 16 prefill chunks of 256 queries over contexts U{256..4096}.
+- 64 query / 8 KV heads, head_dim 128, bf16 cache in 32-token blocks.
+- The step writes the chunks' and the decode tokens' K/V, decodes in
+  512-token partitions (--partition; 0 selects the balanced split), then runs
+  the causal prefill chunks.
+The line carries the decode kernel's HBM roofline (`roofline`), the prefill
+kernel's MFMA roofline (`prefill`), and, timed the same way after the mixed
+step in the same run, the long-context decode of 8 x 32,768 tokens
+(`c3_decode`, skipped with --no-extra).
 
 Consecutive steps read different copies of the pools, at least 1 GiB apart
 in total, so no step is served from the 256 MB Infinity Cache that the
@@ -78,27 +84,34 @@ WORKLOAD_TEXT = {
 }
 
 
-def kernel_source_hash():
+# the kernels whose HBM traffic the committed counter summaries give, with
+# the sources each is built from
+KERNELS = {"decode": ("decode_partition_kernel", ("decode.hip", "pa_internal.h")),
+           "prefill": ("prefill_kernel", ("prefill.hip", "pa_internal.h"))}
+
+
+def kernel_source_hash(kernel="decode"):
     h = hashlib.sha256()
-    for name in ("decode.hip", "pa_internal.h"):
+    for name in KERNELS[kernel][1]:
         with open(os.path.join(ROOT, "paged_kv_cache_424_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def pmc_path(workload):
-    return os.path.join(ROOT, "profiles", f"decode_partition_{workload}_pmc.json")
+def pmc_path(workload, kernel="decode"):
+    stem = "decode_partition" if kernel == "decode" else kernel
+    return os.path.join(ROOT, "profiles", f"{stem}_{workload}_pmc.json")
 
 
-def load_traffic(workload):
-    """HBM bytes per partition-kernel launch from the committed counter summary,
+def load_traffic(workload, kernel="decode"):
+    """HBM bytes per launch of the kernel from the committed counter summary,
     if it was taken on the current kernel source; else None."""
-    path = pmc_path(workload)
+    path = pmc_path(workload, kernel)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         d = json.load(f)
-    if d.get("kernel_source_hash") != kernel_source_hash():
+    if d.get("kernel_source_hash") != kernel_source_hash(kernel):
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -125,14 +138,15 @@ def _mean(rows, pred):
 
 
 def pmc_summary(args):
-    """Write the traffic summary for the decode partition kernel.
+    """Write the traffic summary of one kernel (--kernel decode | prefill).
 
     The calibration kernel is torch's neg over a 1 GiB float32 tensor, which
     reads CALIB_BYTES and writes CALIB_BYTES; each counter is scaled by the
     factor that makes that kernel read exactly its size."""
     fetch = _counter_rows(args.fetch_dir, "FETCH_SIZE")
     write = _counter_rows(args.write_dir, "WRITE_SIZE")
-    is_dec = lambda n: "decode_partition_kernel" in n          # noqa: E731
+    kname = KERNELS[args.kernel][0]
+    is_dec = lambda n: kname in n                               # noqa: E731
     is_cal = lambda n: "neg" in n.lower()                       # noqa: E731
     f_dec, nf = _mean(fetch, is_dec)
     w_dec, nw = _mean(write, is_dec)
@@ -142,8 +156,8 @@ def pmc_summary(args):
     wf = CALIB_BYTES / (w_cal * 1024.0)
     d = {
         "workload": args.workload,
-        "kernel": "decode_partition_kernel",
-        "kernel_source_hash": kernel_source_hash(),
+        "kernel": kname,
+        "kernel_source_hash": kernel_source_hash(args.kernel),
         "dispatches": [nf, nw],
         "fetch_kib_per_launch": f_dec,
         "write_kib_per_launch": w_dec,
@@ -154,39 +168,66 @@ def pmc_summary(args):
         "hbm_bytes_per_launch": f_dec * 1024.0 * ff + w_dec * 1024.0 * wf,
         "command": args.command or "",
     }
-    with open(pmc_path(args.workload), "w") as f:
+    with open(pmc_path(args.workload, args.kernel), "w") as f:
         json.dump(d, f, indent=1)
         f.write("\n")
     print(json.dumps(d))
 
 
 # ---- CPU oracle baseline -----------------------------------------------------------------
-def cpu_baseline(w, nseq, min_seconds=12.0, max_reps=400):
-    """The CPU oracle (fp64, as it stands) decoding the first nseq sequences of
-    the workload, repeated until about min_seconds of CPU work."""
+def cpu_baseline(w, nseq, min_seconds=6.0, max_reps=400, prefill_chunks=2):
+    """The CPU oracle (fp64, as it stands) on a bounded sample of the step.
+
+    Decode: the first nseq sequences, repeated until about min_seconds of CPU
+    work.  With prefill chunks (the mixed step), also every row of the first
+    `prefill_chunks` chunks, once; the step's CPU time is then estimated as
+    the decode time per context token times the step's decode tokens plus the
+    prefill time per (query, visible key) pair times the step's pairs.  The
+    rate is the step's decode tokens over that time, the GPU line's unit."""
     import numpy as np
-    import workloads
     from tests import oracle_run
     try:
         from threadpoolctl import threadpool_info
         blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:                                  # pragma: no cover
         blas = 1
-    sub = workloads.subset(w, w.decode_seqs[:nseq])
-    st = oracle_run.build(sub)
+    cores = len(os.sched_getaffinity(0))
+    st = oracle_run.build(w)
+    seqs = list(range(min(nseq, len(w.decode_seqs))))
+    pairs = None if len(seqs) == len(w.decode_seqs) else [(i, h) for i in seqs for h in range(w.num_q_heads)]
     reps, dt = 0, 0.0
     while reps < max_reps and (reps == 0 or dt < min_seconds):
         t0 = time.perf_counter()
-        out = oracle_run.oracle_decode(sub, st)
+        out = oracle_run.oracle_decode(w, st, pairs=pairs)
         dt += time.perf_counter() - t0
         reps += 1
-    assert np.isfinite(out).all()
-    toks = sum(sub.seq_len(s) for s in sub.decode_seqs)
-    return {"value": reps * toks / dt, "unit": "seq-tokens/s", "cores": int(blas), "kind": "oracle",
-            "sample": f"fp64 numpy oracle decode of {nseq} of {len(w.decode_seqs)} sequences "
-                      f"({toks} context tokens, all {w.num_q_heads} query heads) x {reps}, {dt:.1f} s; "
-                      f"one Python thread driving BLAS with {blas} threads, host cpus "
-                      f"{len(os.sched_getaffinity(0))}"}
+    assert np.isfinite(out[seqs]).all()
+    toks = sum(w.seq_len(w.decode_seqs[i]) for i in seqs)
+    all_toks = sum(w.seq_len(s) for s in w.decode_seqs)
+    per_tok = dt / (reps * toks)
+    sample = (f"fp64 numpy oracle decode of {len(seqs)} of {len(w.decode_seqs)} sequences "
+              f"({toks} context tokens, all {w.num_q_heads} query heads) x {reps}, {dt:.1f} s")
+    step_s = per_tok * all_toks
+    if w.prefill_seqs:
+        stp = st
+        qs = np.concatenate([[0], np.cumsum(w.chunk_len)])
+        n = min(prefill_chunks, len(w.chunk_len))
+        tables, clens = stp.alloc.block_tables(w.prefill_seqs, oracle_run.max_blocks(w))
+        rows = [(t, h) for t in range(int(qs[0]), int(qs[n])) for h in range(w.num_q_heads)]
+        t0 = time.perf_counter()
+        pout = oracle_run.oracle_prefill(w, stp, rows=rows)
+        tp = time.perf_counter() - t0
+        assert np.isfinite(pout[int(qs[0]):int(qs[n])]).all()
+        qk_pairs = lambda cs: sum(C * (int(clens[c]) - C + 1) + C * (C - 1) // 2    # noqa: E731
+                                  for c, C in cs)
+        done = qk_pairs((c, w.chunk_len[c]) for c in range(n))
+        total = qk_pairs(enumerate(w.chunk_len))
+        step_s += tp / done * total
+        sample += (f"; prefill of every (query, head) row of {n} of {len(w.chunk_len)} chunks "
+                   f"({done} of {total} query-key pairs), {tp:.1f} s, scaled to all chunks")
+    sample += f"; one Python thread driving BLAS with {blas} threads on {cores} host cpus"
+    return {"value": all_toks / step_s, "unit": "seq-tokens/s", "cores": cores, "blas_threads": int(blas),
+            "kind": "oracle", "sample": sample}
 
 
 def prefill_flops(w, clens):
@@ -198,50 +239,8 @@ def prefill_flops(w, clens):
     return 4 * w.head_dim * w.num_q_heads * tot
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOAD_TEXT))
-    ap.add_argument("--partition", type=int, default=512,
-                    help="split-K partition in tokens (a multiple of 32), or 0 for the balanced split; "
-                         "default 512, the method's stated partition size")
-    ap.add_argument("--append", choices=["auto", "on", "off"], default="auto",
-                    help="store each decode sequence's newest token inside the decode kernel "
-                         "(pa_decode_append) instead of a separate cache write; auto: when the "
-                         "step writes no other token (a cache-write launch happens anyway otherwise)")
-    ap.add_argument("--overlap", choices=["on", "off"], default="off",
-                    help="run the prefill chunks on a second stream, concurrently with the decode "
-                         "(both wait for the step's cache write); the per-kernel figures are then "
-                         "taken while the two kernels share the chip")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-graph", action="store_true",
-                    help="skip the extra HIP-graph replay measurement of the whole step")
-    ap.add_argument("--cpu-seqs", type=int, default=0, help="sequences in the oracle sample (0 = auto)")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="first run a plain 1 GiB elementwise kernel (scales the HBM byte counters)")
-    ap.add_argument("--pmc-summary", action="store_true",
-                    help="summarise two rocprofv3 --pmc runs (no GPU work) into profiles/")
-    ap.add_argument("--fetch-dir")
-    ap.add_argument("--write-dir")
-    ap.add_argument("--command", help="the profiled command, recorded in the summary")
-    ap.add_argument("--study", choices=["prefix-cache", "fragmentation", "block-size", "batch1", "stream-peak"],
-                    help="run one of the studies in bench_studies.py instead of the benchmark")
-    args = ap.parse_args()
-    if args.pmc_summary:
-        pmc_summary(args)
-        return
-    if args.study:
-        import bench_studies
-        bench_studies.STUDIES[args.study](args)
-        return
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only: the library has no multi-GPU path "
-              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
-        sys.exit(2)
-
+def measure(args, workload):
+    """Time one workload's step; returns the bench line's fields (no CPU baseline)."""
     import numpy as np
     import torch
     import paged_kv_cache_424_amd as pa
@@ -249,8 +248,8 @@ def main():
     from tests import lib_run
 
     torch.cuda.set_device(0)
-    print(f"[bench] workload {args.workload}: generating inputs", file=sys.stderr, flush=True)
-    w = workloads.make(args.workload)
+    print(f"[bench] workload {workload}: generating inputs", file=sys.stderr, flush=True)
+    w = workloads.make(workload)
     st = lib_run.build(w, device="cuda", run_step=True)
     B, Hq, D, H = len(w.decode_seqs), w.num_q_heads, w.head_dim, w.num_kv_heads
     lens = st.lens_host.astype(np.int64)
@@ -462,7 +461,7 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1), bf16 by round-to-nearest-even)",
-        "config": {"workload": WORKLOAD_TEXT[args.workload], "sequences": B,
+        "config": {"workload": WORKLOAD_TEXT[workload], "sequences": B,
                    "context_tokens": tokens, "q_heads": Hq, "kv_heads": H, "head_dim": D,
                    "block_size": w.block_size, "partition": args.partition, "pool_copies": copies,
                    "step": ("copy_blocks + " if pairs else "") +
@@ -472,14 +471,14 @@ def main():
                                                  if pre is not None else "")},
         "roofline": {"bound": "hbm", "kernel": "decode_partition_kernel", "achieved": achieved,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
-                     "traffic": load_traffic(args.workload), "algorithmic_bytes_per_launch": algo,
+                     "traffic": load_traffic(workload), "algorithmic_bytes_per_launch": algo,
                      "avg_launch_us": part_avg_s * 1e6, "median_us": float(np.median(part_ms)) * 1e3,
                      "p10_us": float(np.percentile(part_ms, 10)) * 1e3,
                      "p90_us": float(np.percentile(part_ms, 90)) * 1e3,
                      "timing": "HIP events recorded around the launch call in the timed steps" +
                                (", while the prefill runs on a second stream" if overlap else ""),
                      "avg_launch_us_dispatch_events": float(np.mean(dispatch_ms)) * 1e3,
-                     "kernel_source_hash": kernel_source_hash()},
+                     "kernel_source_hash": kernel_source_hash("decode")},
         "decode_gbs_whole_step": algo / (ms_per_step / 1e3) / 1e9,
         "hip_graph_ms_per_step": graph_ms,
         "prefill_on_second_stream": overlap,
@@ -513,11 +512,77 @@ def main():
                           "p90_us": float(np.percentile(pre_ms, 90)) * 1e3,
                           "timing": "HIP events recorded around the launch call" +
                                     (" on the second stream, while the decode runs" if overlap else ""),
-                          "query_tokens": int(sum(w.chunk_len))}
+                          "query_tokens": int(sum(w.chunk_len)),
+                          "traffic": load_traffic(workload, "prefill"),
+                          "kernel_source_hash": kernel_source_hash("prefill")}
+    return res, w
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c5", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--no-extra", action="store_true",
+                    help="with the mixed step (c5), skip the long-context decode (c3) that the "
+                         "default run times after it")
+    ap.add_argument("--partition", type=int, default=512,
+                    help="split-K partition in tokens (a multiple of 32), or 0 for the balanced split; "
+                         "default 512, the method's stated partition size")
+    ap.add_argument("--append", choices=["auto", "on", "off"], default="auto",
+                    help="store each decode sequence's newest token inside the decode kernel "
+                         "(pa_decode_append) instead of a separate cache write; auto: when the "
+                         "step writes no other token (a cache-write launch happens anyway otherwise)")
+    ap.add_argument("--overlap", choices=["on", "off"], default="off",
+                    help="run the prefill chunks on a second stream, concurrently with the decode "
+                         "(both wait for the step's cache write); the per-kernel figures are then "
+                         "taken while the two kernels share the chip")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the extra HIP-graph replay measurement of the whole step")
+    ap.add_argument("--cpu-seqs", type=int, default=0, help="sequences in the oracle sample (0 = auto)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 1 GiB elementwise kernel (scales the HBM byte counters)")
+    ap.add_argument("--pmc-summary", action="store_true",
+                    help="summarise two rocprofv3 --pmc runs (no GPU work) into profiles/")
+    ap.add_argument("--fetch-dir")
+    ap.add_argument("--write-dir")
+    ap.add_argument("--command", help="the profiled command, recorded in the summary")
+    ap.add_argument("--kernel", choices=sorted(KERNELS), default="decode",
+                    help="with --pmc-summary: the kernel whose counters are summarised")
+    ap.add_argument("--study", choices=["prefix-cache", "fragmentation", "block-size", "batch1", "stream-peak"],
+                    help="run one of the studies in bench_studies.py instead of the benchmark")
+    args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args)
+        return
+    if args.study:
+        import bench_studies
+        bench_studies.STUDIES[args.study](args)
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    res, w = measure(args, args.workload)
+    if args.workload == "c5" and not args.no_extra:
+        # the long-context decode (8 x 32k tokens), timed the same way after the
+        # mixed step: its decode kernel and roofline ride along in this line
+        import torch
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        extra_args = argparse.Namespace(**vars(args))
+        extra_args.overlap = "off"
+        c3, _ = measure(extra_args, "c3")
+        res["c3_decode"] = {k: c3[k] for k in ("value", "unit", "ms_per_step", "config", "roofline",
+                                                 "decode_gbs_whole_step", "hip_graph_ms_per_step",
+                                                 "kernels_us_untimed_pass")}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        nseq = args.cpu_seqs or len(w.decode_seqs)
-        res["cpu_baseline"] = cpu_baseline(w, nseq)
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seqs or len(w.decode_seqs))
     print(json.dumps(res), flush=True)
 
 

@@ -30,7 +30,8 @@ block-size: the Llama-3-8B-shaped decode batch stored with 8, 16, 32, 64 and
     128-token blocks (512-token partitions): partition-kernel time and GB/s
     against the slots left empty in last blocks and the size of the block
     tables.  [studynote 223]
-    section IV, checklist item 1; [ch.09] "한계와 트레이드오프".
+    section IV, checklist item 1; [ch.09] "⚖️ 절충" (small blocks: less
+    fragmentation, more table overhead; large blocks the reverse).
 stream-peak: a plain streaming read (pa_stream_read: one contiguous buffer,
     16-byte non-temporal loads, grid-stride) of the decode workloads' byte
     counts and of 4 GiB, over a few launch shapes: the practical HBM read rate
@@ -38,8 +39,8 @@ stream-peak: a plain streaming read (pa_stream_read: one contiguous buffer,
 batch1: one sequence of 512..32768 tokens, its blocks scattered over the pool
     or laid out in order (identity table), beside 64 sequences of the same
     length: what the indirection and a single sequence cost.  [studynote 223]
-    section III comparison table (slower at batch 1); [velog] closing section
-    (table lookup overhead is small).
+    section IV, "안티패턴" (slower than plain code at batch size 1); [velog]
+    closing section (table lookup overhead is small).
 """
 
 import json

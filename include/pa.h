@@ -33,6 +33,9 @@
  * so one (block, head) tile is contiguous in each pool: K as D/W groups of bs
  * token rows of W channels, V as D channel rows of bs tokens.  pa_kv_offset()
  * evaluates this.
+ *
+ * Calls that measure the library rather than perform the method (kernel
+ * timing, the plain streaming-read yardstick) are declared in pa_measure.h.
  */
 #ifndef PA_H
 #define PA_H
@@ -230,6 +233,10 @@ int pa_allocator_get_stats(const pa_allocator* a, pa_allocator_stats* out);
  *   k_new, v_new:     device [num_tokens][num_kv_heads][head_dim], cache dtype.
  *   slot_mapping:     device int64 [num_tokens]; a negative slot is padding and
  *                     writes nothing; a slot >= num_blocks*block_size is ignored.
+ *                     The non-negative slots must be distinct (the allocator
+ *                     never hands out a slot twice): if two tokens name the same
+ *                     slot, the tokens' stores race and the slot may end up
+ *                     holding elements of either.
  * Bit-exact copy: no arithmetic is applied to the values. */
 int pa_cache_write(void* k_cache, void* v_cache, const pa_cache_desc* desc, const void* k_new,
                    const void* v_new, const int64_t* slot_mapping, int32_t num_tokens,
@@ -239,9 +246,12 @@ int pa_cache_write(void* k_cache, void* v_cache, const pa_cache_desc* desc, cons
  * [velog] "메모리 공유 (Copy-on-Write)"): for each pair, every head and slot of
  * block src is copied to block dst, in both pools.
  *   pairs_host: HOST int64 [n_pairs][2] = (src, dst), as the allocator emits them.
+ *   k_cache, v_cache: 16-byte aligned.
  * PA_ERR_INVALID_ARG (nothing launched) if an id is out of range, a dst repeats,
- * or a dst is also a src.  The ids travel in kernel arguments, so the call makes
- * no host-to-device copy and needs no workspace. */
+ * a dst is also a src, or a pool is misaligned; the check costs O(n_pairs +
+ * num_blocks) host time and num_blocks bytes of host memory (PA_ERR_NO_MEMORY
+ * if those cannot be had).  The ids travel in kernel arguments, so the call
+ * makes no host-to-device copy and needs no workspace. */
 int pa_copy_blocks(void* k_cache, void* v_cache, const pa_cache_desc* desc,
                    const int64_t* pairs_host, int32_t n_pairs, void* stream);
 
@@ -355,18 +365,6 @@ int pa_decode_append_partitions(void* out, int32_t out_dtype, const void* q, con
                                 int32_t partition_size, void* workspace, size_t workspace_bytes,
                                 void* stream);
 
-/* Kernel timing: the next partition pass of the calling host thread (that of
- * pa_decode, pa_decode_append, pa_decode_partitions or
- * pa_decode_append_partitions) records start_event when its first
- * partition-kernel dispatch starts and stop_event when its last one ends
- * (hipExtLaunchKernel's dispatch events, the same clock a kernel trace
- * reports); the request is then cleared.  A call that returns an error before
- * launching leaves it pending.  Events are hipEvent_t values the caller
- * created, on the call's device; either may be NULL (NULL and NULL clears a
- * pending request).  Same kernels, same results; such a launch costs a few
- * microseconds more than a plain one.  Returns PA_OK. */
-int pa_time_next_partitions(void* start_event, void* stop_event);
-
 /* Causal attention of prefill chunks over their paged context, the prefill half
  * of a continuous-batching step ([studynote 223] section IV checklist item 2;
  * [studynote 528] section II, continuous batching table).
@@ -389,34 +387,15 @@ int pa_time_next_partitions(void* start_event, void* stop_event);
  * outside [0, num_blocks) are set to NaN (when they lie inside the output), and
  * nothing is read out of bounds.  Supported: bf16 cache, head_dim 128,
  * num_q_heads/num_kv_heads a power of two up to 16, block_size 8..256 a power
- * of two.  The value pass takes the softmax weights in bf16 (fp32 accumulate),
- * and each row's weight sum is taken from the same bf16 weights. */
+ * of two.  scale must be finite and > 0 (PA_ERR_INVALID_ARG otherwise): the
+ * running maximum is kept on the unscaled logits.  The value pass takes the
+ * softmax weights in bf16 (fp32 accumulate), and each row's weight sum is taken
+ * from the same bf16 weights. */
 int pa_prefill(void* out, int32_t out_dtype, const void* q, const void* k_cache,
                const void* v_cache, const pa_cache_desc* desc, const int32_t* block_tables,
                int32_t max_blocks_per_seq, const int32_t* context_lens,
                const int32_t* query_start_loc, int32_t num_chunks, int32_t num_query_tokens,
                int32_t num_q_heads, int32_t max_query_len, float scale, void* stream);
-
-/* ---- measurement ------------------------------------------------------------------ */
-
-/* A plain streaming read of one contiguous device buffer: the practical HBM
- * read rate of this device, the yardstick beside the spec peak for
- * pa_decode's rate (pa_decode reads the same kind of bytes, scattered over
- * blocks).  Not part of the attention path.
- *   src:           device, 16-byte aligned; bytes a multiple of 16.
- *   blocks_per_cu: workgroups (256 threads) per compute unit, 1..64; the
- *                  grid-stride loop covers any size.
- *   unroll:        independent 16-byte non-temporal loads per thread and loop
- *                  trip: 1, 4, 8 or 16 (PA_ERR_UNSUPPORTED otherwise).
- *   blocked:       0: grid-stride (each load of the grid covers one contiguous
- *                  band, 4 KB per workgroup); 1: each workgroup reads
- *                  unroll x 4 KB contiguous bytes per loop trip.
- *   sink:          device, 4 bytes, written only in the unlikely case that the
- *                  XOR of all words a thread read equals 0x9e3779b9.
- * PA_ERR_INVALID_ARG for a null pointer, misalignment, blocks_per_cu outside
- * 1..64 or blocked not 0 or 1.  Asynchronous on stream. */
-int pa_stream_read(const void* src, size_t bytes, int32_t blocks_per_cu, int32_t unroll, int32_t blocked,
-                   void* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -24,14 +24,15 @@ def paged_waste(length, block_size):
     return blocks * block_size - length
 
 
-def blocks_needed(length, block_size):
-    return -(-length // block_size)
-
-
 def kv_bytes_per_token(num_layers, num_kv_heads, head_dim, bytes_per_elem):
-    """K and V of one token across layers."""
+    """Bytes one token occupies in the cache: a K row and a V row of every kv
+    head, in every layer ([studynote 528] section IV: the per-token KV bytes
+    of the capacity formula)."""
     return 2 * num_layers * num_kv_heads * head_dim * bytes_per_elem
 
 
 def capacity_bytes(max_model_len, batch, kv_bytes_per_tok):
+    """HBM a contiguous cache reserves for `batch` requests of up to
+    max_model_len tokens each ([studynote 528] section IV, capacity planning:
+    max-model-len x batch size x KV bytes per token)."""
     return max_model_len * batch * kv_bytes_per_tok

@@ -101,10 +101,3 @@ def copy_blocks(kpool, vpool, H, bs, D, num_blocks, pairs):
                 kpool[k_index(H, bs, D, dst, g, o, dims)] = kpool[k_index(H, bs, D, src, g, o, dims)]
                 vpool[v_index(H, bs, D, dst, g, o, dims)] = vpool[v_index(H, bs, D, src, g, o, dims)]
 
-
-def read_token(kpool, vpool, H, bs, D, slot, head):
-    """The stored K and V rows of one (slot, head), as stored values."""
-    block, offset = divmod(int(slot), bs)
-    dims = np.arange(D)
-    return (kpool[k_index(H, bs, D, block, head, offset, dims)].copy(),
-            vpool[v_index(H, bs, D, block, head, offset, dims)].copy())

@@ -10,6 +10,8 @@
 // payloads included -- arrives unchanged.  At the sizes a decode step writes
 // they are bound by launch and HBM latency.
 
+#include <vector>
+
 #include "pa_internal.h"
 
 namespace pa {
@@ -174,18 +176,28 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const pa_cache_desc* desc,
     if (!desc_ok(desc) || n_pairs < 0) return PA_ERR_INVALID_ARG;
     if (n_pairs == 0) return PA_OK;
     if (!k_cache || !v_cache || !pairs_host) return PA_ERR_INVALID_ARG;
+    // 16-byte copies of whole (block, all heads) tiles
+    if ((reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache)) % 16)
+        return PA_ERR_INVALID_ARG;
     const int64_t N = desc->num_blocks;
     // Validate the whole list before launching anything: ids in range, no
     // destination twice, no destination that is also a source (so the copies
-    // commute and may run concurrently).
+    // commute and may run concurrently).  One mark per block: O(n_pairs +
+    // num_blocks) for any list.
+    std::vector<uint8_t> is_dst;
+    try {
+        is_dst.assign(static_cast<size_t>(N), 0);
+    } catch (...) {
+        return PA_ERR_NO_MEMORY;
+    }
     for (int32_t i = 0; i < n_pairs; ++i) {
         const int64_t s = pairs_host[2 * i], d = pairs_host[2 * i + 1];
         if (s < 0 || s >= N || d < 0 || d >= N) return PA_ERR_INVALID_ARG;
-        for (int32_t k = 0; k < n_pairs; ++k) {
-            if (k != i && pairs_host[2 * k + 1] == d) return PA_ERR_INVALID_ARG;
-            if (pairs_host[2 * k] == d) return PA_ERR_INVALID_ARG;
-        }
+        if (is_dst[d]) return PA_ERR_INVALID_ARG;
+        is_dst[d] = 1;
     }
+    for (int32_t i = 0; i < n_pairs; ++i)
+        if (is_dst[pairs_host[2 * i]]) return PA_ERR_INVALID_ARG;
     const int64_t tile_bytes = static_cast<int64_t>(desc->num_kv_heads) * desc->block_size *
                                desc->head_dim * static_cast<int64_t>(dtype_size(desc->kv_dtype));
     if (tile_bytes % 16) return PA_ERR_UNSUPPORTED;

@@ -9,6 +9,7 @@
 #include <tuple>
 
 #include "../../include/pa.h"
+#include "../../include/pa_measure.h"
 
 namespace pa {
 

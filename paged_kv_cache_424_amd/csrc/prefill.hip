@@ -36,6 +36,8 @@
 // 16 bytes, V rows by 16 bytes) so that each quarter-wave's 16-byte reads hit
 // 16 different bank groups.
 
+#include <cmath>
+
 #include "pa_internal.h"
 
 namespace pa {
@@ -456,6 +458,9 @@ extern "C" int pa_prefill(void* out, int32_t out_dtype, const void* q, const voi
         max_query_len < 0 || max_blocks_per_seq < 0)
         return PA_ERR_INVALID_ARG;
     if (out_dtype != PA_F32 && out_dtype != PA_BF16) return PA_ERR_INVALID_ARG;
+    // The running max is kept on unscaled logits and raised lazily by
+    // 8 / (scale log2 e): that needs a positive, finite scale.
+    if (!(scale > 0.f) || !std::isfinite(scale)) return PA_ERR_INVALID_ARG;
     const int32_t H = desc->num_kv_heads;
     if (num_q_heads % H) return PA_ERR_INVALID_ARG;
     const int32_t G = num_q_heads / H;

@@ -1,6 +1,6 @@
 """Host-side checks of the C ABI, run without a GPU.
 
-  * the library loads and exports every function include/pa.h declares;
+  * the library loads and exports every function include/*.h declares;
   * the C++ allocator reproduces the oracle's allocator bit-exactly -- tables,
     slots, copy-on-write pairs, counts -- on the pages' worked examples, on
     random op sequences and on every workload's script;
@@ -10,6 +10,7 @@
 """
 
 import ctypes
+import glob
 import os
 import random
 import re
@@ -25,13 +26,15 @@ from oracle import cache
 from oracle.allocator import BlockAllocator, OutOfBlocks, run_script
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "pa.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names.update(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_every_declared_function_is_exported():
@@ -238,6 +241,10 @@ def test_device_calls_reject_bad_host_arguments():
     assert lib.pa_copy_blocks(one, one, ref(desc), pairs.ctypes.data_as(P64), 2, None) == pa.PA_ERR_INVALID_ARG
     pairs = np.array([[1, 8]], dtype=np.int64)              # out of range
     assert lib.pa_copy_blocks(one, one, ref(desc), pairs.ctypes.data_as(P64), 1, None) == pa.PA_ERR_INVALID_ARG
+    pairs = np.array([[1, 2]], dtype=np.int64)              # 16-byte copies: pools must be aligned
+    odd = ctypes.c_void_p(24)
+    assert lib.pa_copy_blocks(odd, one, ref(desc), pairs.ctypes.data_as(P64), 1, None) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_copy_blocks(one, odd, ref(desc), pairs.ctypes.data_as(P64), 1, None) == pa.PA_ERR_INVALID_ARG
     dec = lib.pa_decode
     # q heads not a multiple of kv heads; group too large; bad partition; table too short
     assert dec(one, 0, one, one, one, ref(desc), one, 4, one, 2, 3, 64, 0.1, 0, None, 0, None) == pa.PA_ERR_INVALID_ARG
@@ -282,6 +289,10 @@ def test_device_calls_reject_bad_host_arguments():
     assert pre(one, 0, one, one, one, ref(d128), one, 4, one, one, 1, 8, 6, 8, 0.1, None) == pa.PA_ERR_UNSUPPORTED
     assert pre(one, 0, one, one, one, ref(d128), one, 4, one, one, 1, 8, 3, 8, 0.1, None) == pa.PA_ERR_INVALID_ARG
     assert pre(one, 0, one, one, one, ref(d128), one, 4, one, one, 0, 0, 4, 0, 0.1, None) == pa.PA_OK
+    # the lazily raised running max needs a positive, finite scale
+    for bad_scale in (0.0, -0.1, float("nan"), float("inf")):
+        assert pre(one, 0, one, one, one, ref(d128), one, 4, one, one, 1, 8, 4, 8, bad_scale,
+                   None) == pa.PA_ERR_INVALID_ARG
     for i in range(3):
         ptrs = [one, one, one]
         ptrs[i] = ctypes.c_void_p(24)
@@ -433,3 +444,25 @@ def test_stream_read_rejects_bad_host_arguments():
     assert sr(one, 64, 8, 4, 2, one, None) == pa.PA_ERR_INVALID_ARG
     assert sr(one, 64, 8, 3, 0, one, None) == pa.PA_ERR_UNSUPPORTED
     assert sr(one, 0, 8, 4, 1, one, None) == pa.PA_OK                                  # nothing to read
+
+
+def test_copy_pair_check_is_linear():
+    """A long copy list is validated in one pass: 200,000 valid pairs with one
+    repeated destination at the end are rejected at once (a pairwise check
+    would take 2e10 steps), and nothing is launched."""
+    import time
+    lib = _lib()
+    n = 200_000
+    desc = pa.cache_desc(2 * n + 1, 16, 2, 128, "bf16")
+    pairs = np.stack([np.arange(n), n + np.arange(n)], axis=1).astype(np.int64)
+    pairs[-1, 1] = pairs[0, 1]
+    P64 = ctypes.POINTER(ctypes.c_int64)
+    one = ctypes.c_void_p(16)
+    t0 = time.perf_counter()
+    rc = lib.pa_copy_blocks(one, one, ctypes.byref(desc), pairs.ctypes.data_as(P64), n, None)
+    assert rc == pa.PA_ERR_INVALID_ARG
+    pairs[-1, 1] = 2 * n                                   # now valid except a dst that is a src
+    pairs[5, 0] = pairs[7, 1]
+    rc = lib.pa_copy_blocks(one, one, ctypes.byref(desc), pairs.ctypes.data_as(P64), n, None)
+    assert rc == pa.PA_ERR_INVALID_ARG
+    assert time.perf_counter() - t0 < 1.0

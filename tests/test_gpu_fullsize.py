@@ -4,10 +4,9 @@ and with the balanced split as well.
 
 Everything integer is compared whole and bit for bit: block tables, lengths,
 the step's slots and copy pairs, and both pools byte for byte (never-written
-slots keep their NaN sentinel).  Attention outputs are compared on a sample of
-sequences (every head of each) that the oracle computes one by one: the
-longest, the shortest and seeded random picks; prefill on a sample of query
-rows of every chunk (first, last and random positions).
+slots keep their NaN sentinel).  Attention outputs are compared whole: every
+(sequence, query head) of every decode, at both partition modes, and every
+(query, head) row of every prefill chunk, one test per chunk.
 """
 
 import numpy as np
@@ -41,12 +40,15 @@ def full(request):
     torch.cuda.empty_cache()
 
 
-def _sample_seqs(w, st_l, k=4, seed=0):
-    lens = st_l.lens_host
-    pick = {int(np.argmax(lens)), int(np.argmin(lens))}
-    rng = np.random.default_rng(seed)
-    pick.update(int(x) for x in rng.choice(len(lens), size=min(k, len(lens)), replace=False))
-    return sorted(pick)
+_ORACLE_DECODE = {}
+_GPU_PREFILL = {}
+
+
+def _oracle_decode(name, w, st_o):
+    if name not in _ORACLE_DECODE:
+        _announce(f"oracle decode {name} (full size, every row)")
+        _ORACLE_DECODE[name] = oracle_run.oracle_decode(w, st_o)
+    return _ORACLE_DECODE[name]
 
 
 def test_full_tables_slots_pairs_bit_exact(full):
@@ -69,39 +71,42 @@ def test_full_pools_bit_exact(full):
         assert bad.size == 0, f"{bad.size} elements differ, first at {bad[:5]}"
 
 
-def test_full_decode_sampled(full):
+@pytest.mark.parametrize("part", [BENCH_PARTITION, 0])
+def test_full_decode_every_row(full, part):
     name, w, st_o, st_l = full
-    seqs = _sample_seqs(w, st_l)
-    Hq = w.num_q_heads
-    pairs = [(s, h) for s in seqs for h in range(Hq)]
-    want = oracle_run.oracle_decode(w, st_o, pairs=pairs)[seqs]
-    for part in (BENCH_PARTITION, 0):
-        _announce(f"decode {name} (full size) partition {part}, sequences {seqs}")
-        got = lib_run.decode(w, st_l, partition_size=part).double().cpu().numpy()
-        assert np.isfinite(got).all()
-        err = np.max(np.abs(got[seqs] - want))
-        assert err <= BUDGET, (part, err)
+    want = _oracle_decode(name, w, st_o)
+    assert np.isfinite(want).all()
+    _announce(f"decode {name} (full size) partition {part}, every sequence and head")
+    got = lib_run.decode(w, st_l, partition_size=part).double().cpu().numpy()
+    assert np.isfinite(got).all()
+    err = np.abs(got - want)
+    worst = np.unravel_index(int(np.argmax(err)), err.shape)
+    assert err.max() <= BUDGET, (part, float(err.max()), worst)
+
+
+NCHUNKS_C5 = 16
 
 
 @pytest.mark.parametrize("full", ["c5"], indirect=True)      # the workload with prefill chunks
-def test_full_prefill_sampled(full):
+@pytest.mark.parametrize("chunk", range(NCHUNKS_C5))
+def test_full_prefill_every_row(full, chunk):
+    """Every (query, head) row of one chunk against the oracle."""
     name, w, st_o, st_l = full
-    assert w.prefill_seqs
-    _announce(f"prefill {name} (full size)")
+    assert len(w.chunk_len) == NCHUNKS_C5
+    if name not in _GPU_PREFILL:
+        _announce(f"prefill {name} (full size)")
+        got = lib_run.prefill(w, st_l).double().cpu().numpy()
+        assert np.isfinite(got).all()
+        _GPU_PREFILL[name] = got
+    got = _GPU_PREFILL[name]
     qs = np.concatenate([[0], np.cumsum(w.chunk_len)])
-    rng = np.random.default_rng(1)
-    rows = set()
-    for c in range(len(w.chunk_len)):
-        q0, q1 = int(qs[c]), int(qs[c + 1])
-        for t in {q0, q1 - 1, int(rng.integers(q0, q1))}:
-            for h in rng.choice(w.num_q_heads, size=4, replace=False):
-                rows.add((t, int(h)))
-    rows = sorted(rows)
-    want = oracle_run.oracle_prefill(w, st_o, rows=rows)
-    got = lib_run.prefill(w, st_l).double().cpu().numpy()
-    assert np.isfinite(got).all()
-    t_idx = [t for t, _ in rows]
-    h_idx = [h for _, h in rows]
-    err = np.max(np.abs(got[t_idx, h_idx] - want[t_idx, h_idx]))
-    _announce(f"prefill {name} (full size) sampled max err {err:.2e}")
-    assert err <= 2e-2
+    q0, q1 = int(qs[chunk]), int(qs[chunk + 1])
+    rows = [(t, h) for t in range(q0, q1) for h in range(w.num_q_heads)]
+    _announce(f"oracle prefill {name} chunk {chunk} ({q1 - q0} queries, every head)")
+    want = oracle_run.oracle_prefill(w, st_o, rows=rows)[q0:q1]
+    err = np.abs(got[q0:q1] - want)
+    worst = np.unravel_index(int(np.argmax(err)), err.shape)
+    _announce(f"prefill {name} chunk {chunk} max err {err.max():.2e} at {worst}")
+    # weights enter the value product as bf16 with matching bf16 row sums:
+    # error <= 2^-8 * max|v| (max|v| < 6 for N(0,1) draws of this size)
+    assert err.max() <= 2e-2, (chunk, float(err.max()), worst)

@@ -277,31 +277,58 @@ def _run_both(w):
     return oracle_run.oracle_decode(w, st_o), lib_run.decode(w, st_l).double().cpu().numpy()
 
 
-def test_needle_in_every_logical_block():
-    base = workloads.make("c3", small=True)       # 2 x 3000 tokens, several partitions
-    bs, G, D = base.block_size, base.group, base.head_dim
-    q = np.zeros((2, base.num_q_heads, D), dtype=np.float32)
-    q[:, :, 0] = 1.0                               # every head looks along channel 0
+@pytest.mark.parametrize("part", [512, 0])
+def test_needle_in_every_logical_block(part):
+    """Every logical block of every sequence and kv head holds one needle key,
+    and across the calls every needle is selected by some query head.
+
+    Block b's needle key is 200 * sign_b * e_{b mod 128} (sign_b = -1 for
+    b >= 128), at an offset inside the block that varies with b and the head;
+    all other keys are 0.  A query head that looks along +-e_c gives block b's
+    needle a logit of 200/sqrt(128) ~ 17.7 and every other key 0 or -17.7, so
+    its output is that needle's value row within L * exp(-17.7) ~ 1e-4 of its
+    scale ([ch.09] "해법": block j of the table is position range j of the
+    contiguous context, whichever physical block holds it).  Needle values are
+    small integers that differ between neighbouring blocks in every channel."""
+    base = workloads.make("c3", small=True)       # 2 x 3000 tokens: 188 blocks per sequence
+    bs, G, D, H = base.block_size, base.group, base.head_dim, base.num_kv_heads
+    B, Hq = len(base.decode_seqs), base.num_q_heads
     k = np.zeros(base.k_tok.shape, dtype=np.float32)
     v = np.zeros(base.v_tok.shape, dtype=np.float32)
-    # sequence s, kv head g: the needle sits in logical block (7*s + 3*g + 1) mod nblocks
-    needles = {}
-    for s in range(2):
+    nblk = {}
+    needle_v = {}
+    for si, s in enumerate(base.decode_seqs):
         rows = base.tok_rows[s]
-        nb = -(-len(rows) // bs)
-        for g in range(base.num_kv_heads):
-            blk = (7 * s + 3 * g + 1) % nb
-            pos = min(blk * bs + (g % bs), len(rows) - 1)
-            k[rows[pos], g, 0] = 200.0             # logit 200/sqrt(128) ~ 17.7 above all others
-            v[rows[pos], g, :] = np.arange(D) + 10 * g + 1000 * s
-            needles[(s, g)] = v[rows[pos], g, :].copy()
-    w = _probe_workload(base, k=_bf16(k), v=_bf16(v), q=_bf16(q))
-    want, got = _run_both(w)
-    assert np.max(np.abs(got - want)) <= 2e-4 * np.abs(want).max()
-    for (s, g), vec in needles.items():
-        for h in range(g * G, (g + 1) * G):
-            # weight of the needle >= 1 - L*exp(-17.7): the output is its value row
-            assert np.allclose(got[s, h], vec.astype(np.float64), rtol=0, atol=1e-2 * np.abs(vec).max())
+        L = len(rows)
+        nb = -(-L // bs)
+        assert nb <= 2 * D
+        nblk[si] = nb
+        for g in range(H):
+            for b in range(nb):
+                pos = min(b * bs + (5 * b + 3 * g) % bs, L - 1)
+                k[rows[pos], g, b % D] = 200.0 if b < D else -200.0
+                v[rows[pos], g, :] = ((37 * b + 11 * np.arange(D) + 5 * g + 3 * si) % 64) - 32
+                needle_v[(si, g, b)] = v[rows[pos], g, :].astype(np.float64)
+    w = _probe_workload(base, k=_bf16(k), v=_bf16(v))
+    st_l = lib_run.build(w)
+    ncalls = -(-max(nblk.values()) // G)
+    seen = set()
+    for call in range(ncalls):
+        q = np.zeros((B, Hq, D), dtype=np.float32)
+        target = {}
+        for si in range(B):
+            for h in range(Hq):
+                b = (call * G + h % G) % nblk[si]
+                q[si, h, b % D] = 1.0 if b < D else -1.0
+                target[(si, h)] = b
+        qd = lib_run.torch_stored(_bf16(q), w.dtype).cuda()
+        got = lib_run.decode(w, st_l, partition_size=part, q=qd).double().cpu().numpy()
+        for (si, h), b in target.items():
+            want = needle_v[(si, h // G, b)]
+            err = np.max(np.abs(got[si, h] - want))
+            assert err <= 1e-3 * 32, (part, call, si, h, b, err)
+            seen.add((si, h // G, b))
+    assert seen == set(needle_v)                  # every block of every (sequence, kv head)
 
 
 def test_constant_values_per_kv_head_and_ones():
@@ -445,3 +472,29 @@ def test_cache_write_runs_and_scattered_slots(dtype, bs, D):
         got = lib_run.pool_bits(dev, dtype)
         want = host.view(np.uint16 if dtype == "bf16" else np.uint32)
         assert np.array_equal(got, want)
+
+
+def test_copy_blocks_4096_pairs_bit_exact():
+    """A long copy-on-write list (4,096 pairs, more than one launch's batch):
+    both pools bit-exact against the oracle's copies, every other block
+    untouched."""
+    import paged_kv_cache_424_amd as pa
+    from oracle import cache
+    H, bs, D, N, n = 2, 16, 128, 9000, 4096
+    rng = np.random.default_rng(4096)
+    blocks = rng.permutation(N)
+    src = rng.choice(blocks[:N - n], size=n, replace=True)     # sources may repeat
+    dst = blocks[N - n:]                                        # distinct, never a source
+    pairs = np.stack([src, dst], axis=1).astype(np.int64)
+    _announce(f"copy_blocks {n} pairs, pool {N} blocks")
+    kbits = rng.integers(0, 1 << 16, size=N * H * bs * D, dtype=np.uint16)
+    vbits = rng.integers(0, 1 << 16, size=N * H * bs * D, dtype=np.uint16)
+    desc = pa.cache_desc(N, bs, H, D, "bf16")
+    kc = torch.from_numpy(kbits.view(np.int16).copy()).cuda().view(torch.bfloat16)
+    vc = torch.from_numpy(vbits.view(np.int16).copy()).cuda().view(torch.bfloat16)
+    pa.pa_copy_blocks(kc, vc, desc, pairs)
+    torch.cuda.synchronize()
+    kw, vw = kbits.copy(), vbits.copy()
+    cache.copy_blocks(kw, vw, H, bs, D, N, [tuple(p) for p in pairs.tolist()])
+    assert np.array_equal(lib_run.pool_bits(kc, "bf16"), kw)
+    assert np.array_equal(lib_run.pool_bits(vc, "bf16"), vw)

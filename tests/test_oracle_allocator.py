@@ -12,7 +12,7 @@ import random
 
 import pytest
 
-from oracle import accounting
+from oracle import accounting, cache
 from oracle.allocator import BlockAllocator, OutOfBlocks, BadBlock, BadSequence, run_script
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "allocator_examples.json")
@@ -120,6 +120,44 @@ def test_fragmentation_examples(golden):
     assert accounting.contiguous_waste(g["reserved"], g["used"]) == g["expected_waste"]
     g = golden["studynote223_block_size"]
     assert accounting.paged_waste(g["used"], g["block_size"]) == g["expected_empty"]
+
+
+def _capacity_pins(acc):
+    """The capacity formula of [studynote 528] section IV (HBM = max-model-len
+    x batch x KV bytes per token), pinned two ways that do not use its code."""
+    # hand-worked: head_dim 128, 8 kv heads, bf16, one layer -> K row 256 B +
+    # V row 256 B per head, 8 heads: 4,096 B per token; the page's
+    # --max-model-len 8192 at a batch of 64: 8192 * 64 * 4096 B = 2 GiB
+    assert acc.kv_bytes_per_token(1, 8, 128, 2) == 4096
+    assert acc.capacity_bytes(8192, 64, acc.kv_bytes_per_token(1, 8, 128, 2)) == 2 << 30
+    # 80 layers of that head shape: 320 KiB per token, 160 GiB for the same reservation
+    assert acc.kv_bytes_per_token(80, 8, 128, 2) == 320 * 1024
+    assert acc.capacity_bytes(8192, 64, acc.kv_bytes_per_token(80, 8, 128, 2)) == 160 << 30
+    # against the size of real pools: a K pool and a V pool (numpy arrays of
+    # the stored dtype) with exactly max_len * batch token slots per layer
+    for dtype, b in (("bf16", 2), ("f32", 4)):
+        for H, D, bs, max_len, batch, layers in ((8, 128, 16, 64, 3, 1), (2, 64, 8, 40, 5, 3)):
+            nblk = max_len * batch // bs
+            pools = [cache.new_pool(nblk, H, bs, D, dtype, 0) for _ in range(2 * layers)]
+            assert sum(p.nbytes for p in pools) == \
+                acc.capacity_bytes(max_len, batch, acc.kv_bytes_per_token(layers, H, D, b))
+
+
+def test_capacity_formula_pins():
+    _capacity_pins(accounting)
+
+
+def test_planted_capacity_slips_are_caught(monkeypatch):
+    real = accounting.kv_bytes_per_token
+    # K+V counted once instead of twice
+    monkeypatch.setattr(accounting, "kv_bytes_per_token", lambda L, H, D, b: real(L, H, D, b) // 2)
+    with pytest.raises(AssertionError):
+        _capacity_pins(accounting)
+    monkeypatch.setattr(accounting, "kv_bytes_per_token", real)
+    # the batch factor dropped
+    monkeypatch.setattr(accounting, "capacity_bytes", lambda m, bt, k: m * k)
+    with pytest.raises(AssertionError):
+        _capacity_pins(accounting)
 
 
 def test_stats_worked_example():
