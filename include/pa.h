@@ -55,7 +55,8 @@ typedef enum pa_status {
     PA_ERR_BAD_SEQ = -4,       /* unknown sequence id */
     PA_ERR_HIP = -5,           /* a HIP runtime call or kernel launch failed */
     PA_ERR_UNSUPPORTED = -6,   /* valid, but a shape the library has no kernel for */
-    PA_ERR_NO_MEMORY = -7      /* host allocation failed */
+    PA_ERR_NO_MEMORY = -7,     /* host allocation failed */
+    PA_ERR_TOO_LARGE = -8      /* the call needs more than a fixed limit of the library */
 } pa_status;
 
 typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
@@ -364,6 +365,27 @@ int pa_decode_append_partitions(void* out, int32_t out_dtype, const void* q, con
                                 int32_t num_q_heads, int32_t max_context_len, float scale,
                                 int32_t partition_size, void* workspace, size_t workspace_bytes,
                                 void* stream);
+
+/* pa_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same kernels and results as pa_decode with the same arguments, but the
+ * split-K workspace is a fixed array inside the library
+ * (PA_DECODE_NO_ALLOC_MAX_WORKSPACE bytes per device, held from the first call
+ * on a device until the process ends) instead of caller memory.  The call
+ * allocates nothing; the caller still passes q, the pools, tables, lengths and
+ * out.  PA_ERR_TOO_LARGE (nothing launched) when
+ * pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
+ * partition_size) exceeds the limit: with 512-token partitions, for instance,
+ * 240 sequences x 64 query heads x 8,192 tokens at head_dim 128 fit.  Every
+ * call on one device shares that device's array (its contents before a call do
+ * not matter): calls that overlap in time on one device -- on different
+ * streams, or from different host threads -- race and must not be made. */
+#define PA_DECODE_NO_ALLOC_MAX_WORKSPACE ((size_t)128 << 20)
+int pa_decode_no_alloc(void* out, int32_t out_dtype, const void* q, const void* k_cache,
+                       const void* v_cache, const pa_cache_desc* desc, const int32_t* block_tables,
+                       int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                       int32_t num_q_heads, int32_t max_context_len, float scale,
+                       int32_t partition_size, void* stream);
 
 /* Causal attention of prefill chunks over their paged context, the prefill half
  * of a continuous-batching step ([studynote 223] section IV checklist item 2;

@@ -48,6 +48,10 @@ PA_ERR_BAD_SEQ = -4
 PA_ERR_HIP = -5
 PA_ERR_UNSUPPORTED = -6
 PA_ERR_NO_MEMORY = -7
+PA_ERR_TOO_LARGE = -8
+
+# workspace limit of pa_decode_no_alloc (its fixed per-device array)
+PA_DECODE_NO_ALLOC_MAX_WORKSPACE = 128 << 20
 
 PA_F32 = 0
 PA_BF16 = 1
@@ -125,6 +129,7 @@ _sig("pa_decode_workspace_bytes", _sz, _i32, _i32, _i32, _i32, _i32)
 _DEC = [_vp, _i32, _vp, _vp, _vp, _PD, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]
 _sig("pa_decode", ctypes.c_int, *_DEC)
 _sig("pa_decode_partitions", ctypes.c_int, *_DEC)
+_sig("pa_decode_no_alloc", ctypes.c_int, *_DEC[:14], _vp)
 _sig("pa_decode_reduce", ctypes.c_int, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp)
 _sig("pa_time_next_partitions", ctypes.c_int, _vp, _vp)
 _DEC_APPEND = [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _PD, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _i32,
@@ -373,6 +378,14 @@ def pa_decode(out, q, k_cache, v_cache, desc, block_tables, context_lens, max_co
     _check(_lib.pa_decode(*_decode_args(out, q, k_cache, v_cache, desc, block_tables, context_lens,
                                         max_context_len, scale, partition_size, workspace, stream)),
            "pa_decode")
+
+
+def pa_decode_no_alloc(out, q, k_cache, v_cache, desc, block_tables, context_lens, max_context_len, scale,
+                       partition_size=0, stream=None):
+    """pa_decode with the library's fixed per-device workspace (no allocation)."""
+    d = _decode_args(out, q, k_cache, v_cache, desc, block_tables, context_lens, max_context_len, scale,
+                     partition_size, None, stream)
+    _check(_lib.pa_decode_no_alloc(*d[:14], d[16]), "pa_decode_no_alloc")
 
 
 def pa_decode_partitions(out, q, k_cache, v_cache, desc, block_tables, context_lens, max_context_len,

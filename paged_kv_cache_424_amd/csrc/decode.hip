@@ -63,6 +63,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "pa_internal.h"
 
@@ -1070,3 +1071,69 @@ int pa_decode(void* out, int32_t out_dtype, const void* q, const void* k_cache, 
 }
 
 }  // extern "C"
+
+// ---- decode without allocation --------------------------------------------------------
+// For callers that cannot allocate device memory (code under graph capture,
+// tight serving loops, harnesses that forbid hipMalloc): pa_decode with the
+// workspace in this fixed array instead of caller memory.  Every device the
+// library runs on holds its own copy for the life of the process.  In host
+// code the array's name is only a stand-in: its device address, looked up once
+// per device, is what the kernels are given.
+static __device__ __align__(256) unsigned char scratch[PA_DECODE_NO_ALLOC_MAX_WORKSPACE];
+
+namespace pa {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up on the first
+// call for each device).
+int scratch_address(void** out) {
+    int dev = 0;
+    int rc = hip_status(hipGetDevice(&dev));
+    if (rc != PA_OK) return rc;
+    if (dev < 0 || dev >= kMaxDevices) return PA_ERR_UNSUPPORTED;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            rc = hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+            if (rc != PA_OK) return rc;
+            if (!p) return PA_ERR_HIP;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return PA_OK;
+}
+
+}  // namespace
+}  // namespace pa
+
+extern "C" int pa_decode_no_alloc(void* out, int32_t out_dtype, const void* q, const void* k_cache,
+                                  const void* v_cache, const pa_cache_desc* desc,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t max_context_len, float scale, int32_t partition_size,
+                                  void* stream) {
+    // argument checks of pa_decode first (no device is touched for a bad call)
+    pa::Plan c;
+    int rc = pa::check_decode(desc, out_dtype, num_seqs, num_q_heads, max_blocks_per_seq,
+                              max_context_len, partition_size, &c);
+    if (rc != PA_OK) return rc;
+    const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, desc->head_dim,
+                                                  max_context_len, partition_size);
+    if (need > PA_DECODE_NO_ALLOC_MAX_WORKSPACE) return PA_ERR_TOO_LARGE;
+    if (num_seqs == 0) return PA_OK;
+    void* ws = nullptr;
+    if (need > 0) {
+        rc = pa::scratch_address(&ws);
+        if (rc != PA_OK) return rc;
+    }
+    return pa_decode(out, out_dtype, q, k_cache, v_cache, desc, block_tables, max_blocks_per_seq,
+                     context_lens, num_seqs, num_q_heads, max_context_len, scale, partition_size, ws,
+                     need, stream);
+}

@@ -22,6 +22,7 @@ const char* pa_status_string(int status) {
         case PA_ERR_HIP: return "HIP runtime error";
         case PA_ERR_UNSUPPORTED: return "unsupported shape";
         case PA_ERR_NO_MEMORY: return "host out of memory";
+        case PA_ERR_TOO_LARGE: return "request exceeds a fixed limit of the library";
         default: return "unknown status";
     }
 }

@@ -466,3 +466,23 @@ def test_copy_pair_check_is_linear():
     rc = lib.pa_copy_blocks(one, one, ctypes.byref(desc), pairs.ctypes.data_as(P64), n, None)
     assert rc == pa.PA_ERR_INVALID_ARG
     assert time.perf_counter() - t0 < 1.0
+
+
+def test_no_alloc_decode_rejects_beyond_its_limit_without_a_device():
+    """pa_decode_no_alloc checks its arguments and its workspace limit before it
+    touches a device: a request beyond the fixed array is PA_ERR_TOO_LARGE."""
+    lib = _lib()
+    desc = pa.cache_desc(8, 16, 8, 128, "bf16")
+    one = ctypes.c_void_p(16)
+    big_ctx = 1 << 20
+    args = lambda B, ctx, part: (one, 0, one, one, one, ctypes.byref(desc), one, ctx // 16, one, B, 64,  # noqa: E731
+                                 ctx, 0.1, part, None)
+    assert pa.pa_decode_workspace_bytes(64, 64, 128, big_ctx, 512) > pa.PA_DECODE_NO_ALLOC_MAX_WORKSPACE
+    assert lib.pa_decode_no_alloc(*args(64, big_ctx, 512)) == pa.PA_ERR_TOO_LARGE
+    assert lib.pa_decode_no_alloc(*args(64, big_ctx, 0)) == pa.PA_ERR_TOO_LARGE
+    # pa_decode's own checks come first
+    assert lib.pa_decode_no_alloc(*args(64, big_ctx, 48)) == pa.PA_ERR_UNSUPPORTED
+    assert lib.pa_decode_no_alloc(*args(0, 64, 512)) == pa.PA_OK          # empty batch: nothing to do
+    # the limit admits the mixed step's decode: 240 sequences x 64 heads x 8,192 tokens at 512
+    assert pa.pa_decode_workspace_bytes(240, 64, 128, 8192, 512) <= pa.PA_DECODE_NO_ALLOC_MAX_WORKSPACE
+    assert pa.pa_status_string(pa.PA_ERR_TOO_LARGE) != "unknown status"
