@@ -17,7 +17,9 @@ import numpy as np
 import torch  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpa.so")
+# PA_LIBRARY names another build of the same library to load instead (the
+# sanitizer build of build.py --sanitize); by default the in-tree libpa.so.
+LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(_HERE, "libpa.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(

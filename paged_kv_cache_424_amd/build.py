@@ -1,12 +1,18 @@
 """Build the HIP library libpa.so in-tree for gfx950.
 
-    python paged_kv_cache_424_amd/build.py
+    python paged_kv_cache_424_amd/build.py             # libpa.so
+    python paged_kv_cache_424_amd/build.py --sanitize  # _build/sanitize/libpa.so
 
 (run it as a script: importing the package first would load the old library)
 
 Host-only C++ (allocator, layout) is compiled with g++; the HIP sources with
 hipcc --offload-arch=gfx950.  Packed-fp32 instruction selection is turned off
 for the device code (-packed-fp32-ops).  Always recompiles.
+
+--sanitize builds a second copy of the library whose host-only C++ (the block
+allocator, prefix cache and layout) is instrumented with AddressSanitizer and
+UndefinedBehaviorSanitizer (g++; the HIP objects are the regular ones), for
+CPU test runs: load it with PA_LIBRARY=<path> and LD_PRELOAD=<g++'s libasan>.
 """
 
 import concurrent.futures
@@ -27,6 +33,8 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
+SAN_LIB = os.path.join(BUILD, "sanitize", "libpa.so")
 
 
 def _hipcc():
@@ -65,5 +73,28 @@ def build(verbose=False):
     return LIB
 
 
+def build_sanitized():
+    """The library with ASan/UBSan-instrumented host C++ (see the module doc).
+    Reuses the regular build's HIP objects, building them first if missing."""
+    hip_objs = [os.path.join(BUILD, os.path.basename(src) + ".o")
+                for src in sorted(glob.glob(os.path.join(CSRC, "*.hip")))]
+    if not all(os.path.exists(o) for o in hip_objs):
+        build()
+    out_dir = os.path.dirname(SAN_LIB)
+    os.makedirs(out_dir, exist_ok=True)
+    objs = []
+    for src in sorted(glob.glob(os.path.join(CSRC, "*.cpp"))):
+        obj = os.path.join(out_dir, os.path.basename(src) + ".o")
+        _run(["g++", "-O1", "-std=c++17", "-fPIC", *SAN_FLAGS, "-c", src, "-o", obj])
+        objs.append(obj)
+    tmp = SAN_LIB + ".tmp"
+    _run(["g++", "-shared", *SAN_FLAGS, "-o", tmp, *objs, *hip_objs, "-L/opt/rocm/lib", "-lamdhip64"])
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--sanitize" in sys.argv:
+        print(build_sanitized())
+    else:
+        print(build(verbose="-v" in sys.argv))

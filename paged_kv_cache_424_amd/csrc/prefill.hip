@@ -272,12 +272,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     auto load_tile = [&](int t, const int64_t* offs, int buf) {
         // the tile's offset inside its block (only for blocks larger than a tile)
         const int in_blk = big_blocks ? ((t * kKT) & (bs - 1)) : 0;
+        // all eight block offsets are read before the first load: each load is
+        // an asm statement that orders memory, so a read placed after one would
+        // wait for it and the reads' latencies would add up
+        int64_t ok[4], ov[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) ok[p] = offs[kslot[p]];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) ov[p] = offs[vslot[p]];
 #pragma unroll
         for (int p = 0; p < 4; ++p)
-            load_to_lds(kbase + offs[kslot[p]] + koff[p] + in_blk * 32 * 2, &sK[buf][(16 * w + 4 * p) * kD]);
+            load_to_lds(kbase + ok[p] + koff[p] + in_blk * 32 * 2, &sK[buf][(16 * w + 4 * p) * kD]);
 #pragma unroll
         for (int p = 0; p < 4; ++p)
-            load_to_lds(vbase + offs[vslot[p]] + voff[p] + in_blk * 2, &sV[buf][(32 * w + 8 * p) * kKT]);
+            load_to_lds(vbase + ov[p] + voff[p] + in_blk * 2, &sV[buf][(32 * w + 8 * p) * kKT]);
     };
     f32x16_t acc[kMT];
 #pragma unroll
@@ -414,9 +422,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 }
             }
         }
+        wait_loads();                             // this wave's share of tile kt + 1 is in LDS
+        // The id of tile kt + 2 was loaded after tile kt + 1's loads, so its
+        // check needs them all to have landed: keep it behind the wait, where
+        // the scheduler cannot hoist it (and the wait with it) into the value
+        // products above.
+        __builtin_amdgcn_sched_barrier(0);
         const int id = checked(nb_idx, nid);
         if (next_ids && tid < n_ids) s_off[buf][tid] = id * tile_bytes;
-        wait_loads();                             // this wave's share of tile kt + 1 is in LDS
         if (kt + 2 == nkt) zero_v_tail(buf ^ 1, kt + 1);
         __syncthreads();
     }

@@ -21,10 +21,13 @@ def _announce(msg):
     print(f"[gpu-case] {msg}", flush=True)
 
 
-@pytest.mark.parametrize("name,part", [("c2", 0), ("c2", 512), ("c3", 256), ("c1", 128)])
-def test_decode_graph_replays_match_eager(name, part):
-    _announce(f"graph decode {name} part {part}")
-    w = workloads.make(name, small=True)
+@pytest.mark.parametrize("name,part,small", [("c2", 0, True), ("c2", 512, True), ("c3", 256, True),
+                                             ("c1", 128, True), ("c2", 0, False)])
+def test_decode_graph_replays_match_eager(name, part, small):
+    # the full-size batch runs the balanced split with dynamic cells: each
+    # replay must find its cell counters reset by the one before
+    _announce(f"graph decode {name} part {part} small {small}")
+    w = workloads.make(name, small=small)
     st = lib_run.build(w)
     B, Hq, D = st.q.shape
     eager = lib_run.decode(w, st, partition_size=part)

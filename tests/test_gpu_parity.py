@@ -103,23 +103,31 @@ def test_many_sequences_and_skewed_lengths():
         assert np.max(np.abs(got - want)) <= BUDGET["bf16"], part
 
 
-def test_workspace_contents_do_not_matter():
+@pytest.mark.parametrize("small", [True, False])
+def test_workspace_contents_do_not_matter(small):
     # the workspace is scratch: whatever it holds before a call (and between
-    # calls) must not change the result
+    # calls) must not change the result; at full size the balanced split
+    # claims dynamic cells through counters kept in the workspace, so random
+    # bytes there (any tag, any count) must be recognised as stale
     import paged_kv_cache_424_amd as pa
-    w = workloads.make("c2", small=True)
+    w = workloads.make("c2", small=small)
     st = lib_run.build(w)
     B, Hq, D = st.q.shape
     ref = lib_run.decode(w, st)
     wsb = pa.pa_decode_workspace_bytes(B, Hq, D, st.max_ctx, 0)
-    for fill in (0, 0xFF, 0x7F):
-        ws = torch.full((wsb,), fill, dtype=torch.uint8, device="cuda")
+    rng = np.random.default_rng(7)
+    fills = [0, 0xFF, 0x7F] + [torch.from_numpy(rng.integers(0, 256, size=wsb, dtype=np.uint8))]
+    for fill in fills:
+        if isinstance(fill, int):
+            ws = torch.full((wsb,), fill, dtype=torch.uint8, device="cuda")
+        else:
+            ws = fill.cuda()
         for rep in range(2):
             out = torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
             pa.pa_decode(out, st.q, st.kc, st.vc, st.desc, st.tables, st.lens, st.max_ctx, w.scale,
                          workspace=ws)
             torch.cuda.synchronize()
-            assert torch.equal(out, ref), (fill, rep)
+            assert torch.equal(out, ref), (str(fill)[:20], rep)
 
 
 # ---- invariances: bit-identical outputs ----------------------------------------------
