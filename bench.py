@@ -23,13 +23,13 @@ the largest configuration that fits one GPU.
 - 240 decode sequences, lognormal context lengths (median 1024, [64, 8192]),
   plus 16 prefill chunks of 256 queries over contexts U{256..4096}.
 - 64 query / 8 KV heads, head_dim 128, bf16 cache in 32-token blocks.
-- The step writes the chunks' and the decode tokens' K/V, decodes in
-  512-token partitions (--partition; 0 selects the balanced split), then runs
-  the causal prefill chunks.
+- The step writes the chunks' and the decode tokens' K/V, decodes with the
+  balanced split (--partition P selects P-token partitions), then runs the
+  causal prefill chunks.
 The line carries the decode kernel's HBM roofline (`roofline`), the prefill
 kernel's MFMA roofline (`prefill`), and, timed the same way after the mixed
-step in the same run, the long-context decode of 8 x 32,768 tokens
-(`c3_decode`, skipped with --no-extra).
+step in the same run, the long-context decode of 8 x 32,768 tokens in its
+stated 512-token partitions (`c3_decode`, skipped with --no-extra).
 
 Consecutive steps read different copies of the pools, at least 1 GiB apart
 in total, so no step is served from the 256 MB Infinity Cache that the
@@ -239,8 +239,14 @@ def prefill_flops(w, clens):
     return 4 * w.head_dim * w.num_q_heads * tot
 
 
+DEFAULT_PARTITION = {"c5": 0}          # every other workload: 512 tokens
+
+
 def measure(args, workload):
     """Time one workload's step; returns the bench line's fields (no CPU baseline)."""
+    if args.partition is None:
+        args = argparse.Namespace(**vars(args))
+        args.partition = DEFAULT_PARTITION.get(workload, 512)
     import numpy as np
     import torch
     import paged_kv_cache_424_amd as pa
@@ -527,9 +533,11 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="with the mixed step (c5), skip the long-context decode (c3) that the "
                          "default run times after it")
-    ap.add_argument("--partition", type=int, default=512,
+    ap.add_argument("--partition", type=int, default=None,
                     help="split-K partition in tokens (a multiple of 32), or 0 for the balanced split; "
-                         "default 512, the method's stated partition size")
+                         "default: the long-context decode's stated 512-token partitions for c3, the "
+                         "balanced split for the mixed step (c5 states no partition size; measured "
+                         "faster there), 512 otherwise (measured faster on c2)")
     ap.add_argument("--append", choices=["auto", "on", "off"], default="auto",
                     help="store each decode sequence's newest token inside the decode kernel "
                          "(pa_decode_append) instead of a separate cache write; auto: when the "

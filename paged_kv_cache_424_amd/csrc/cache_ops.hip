@@ -29,14 +29,26 @@ namespace {
 // neighbouring channels of one token row.
 constexpr int kGroupTokens = 8;
 
+// Workgroup -> (token group, kv head).  The grid is one-dimensional and
+// remapped so that consecutive token groups of one head run on the same XCD:
+// the groups of one block write disjoint 16-byte pieces of the same V channel
+// rows, and when those pieces meet in one L2 they leave it as whole lines
+// instead of partial writes from several XCDs.
+__device__ __forceinline__ void group_and_head(int ngroups, int64_t* t0, int* g) {
+    const int u = xcd_remap(blockIdx.x, gridDim.x);
+    *g = u / ngroups;
+    *t0 = static_cast<int64_t>(u % ngroups) * kGroupTokens;
+}
+
 template <typename W>   // W = uint16_t (bf16) or uint32_t (fp32): the element's bits
 __global__ __launch_bounds__(256) void cache_write_kernel(
     W* __restrict__ kc, W* __restrict__ vc, const W* __restrict__ kn, const W* __restrict__ vn,
     const int64_t* __restrict__ slots, int32_t num_tokens, int32_t H, int32_t D, int32_t bs,
     int64_t num_slots) {
-    const int g = blockIdx.y;
+    int g;
+    int64_t t0;
+    group_and_head((num_tokens + kGroupTokens - 1) / kGroupTokens, &t0, &g);
     const int tid = threadIdx.x;
-    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kGroupTokens;
     const int nt = static_cast<int>(min(static_cast<int64_t>(kGroupTokens), num_tokens - t0));
 
     // K: channel group slowest, then token, then channel within the group
@@ -76,9 +88,10 @@ __global__ __launch_bounds__(256) void cache_write_vec_kernel(
     constexpr int EPV = 16 / sizeof(W);                    // elements per 16-byte piece
     __shared__ int64_t s_slot[kGroupTokens];
     __shared__ __align__(16) W s_v[kGroupTokens * 128 * 4 / sizeof(W)];   // D * sizeof(W) <= 512 bytes
-    const int g = blockIdx.y;
+    int g;
+    int64_t t0;
+    group_and_head((num_tokens + kGroupTokens - 1) / kGroupTokens, &t0, &g);
     const int tid = threadIdx.x;
-    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kGroupTokens;
     const int nt = static_cast<int>(min(static_cast<int64_t>(kGroupTokens), num_tokens - t0));
     const int pieces = D / EPV;                            // per token row
     if (tid < nt) s_slot[tid] = slots[t0 + tid];
@@ -143,9 +156,9 @@ int pa_cache_write(void* k_cache, void* v_cache, const pa_cache_desc* desc, cons
     const int32_t H = desc->num_kv_heads, D = desc->head_dim, bs = desc->block_size;
     const int64_t num_slots = static_cast<int64_t>(desc->num_blocks) * bs;
     const int64_t groups = (static_cast<int64_t>(num_tokens) + kGroupTokens - 1) / kGroupTokens;
-    if (groups > INT32_MAX || H > 65535) return PA_ERR_UNSUPPORTED;
+    if (groups * H > INT32_MAX) return PA_ERR_UNSUPPORTED;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const dim3 grid(static_cast<uint32_t>(groups), static_cast<uint32_t>(H));
+    const dim3 grid(static_cast<uint32_t>(groups * H));
     const bool aligned = ((reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache) |
                            reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15) == 0;
     if (aligned && D % 32 == 0 && D <= 128) {
