@@ -242,6 +242,33 @@ def prefill_flops(w, clens):
 DEFAULT_PARTITION = {"c5": 0}          # every other workload: 512 tokens
 
 
+def attention_loop_ceiling(prefill_tflops, iters=1000, reps=3):
+    """TFLOP/s of pa_attention_loop_peak in its three modes (HIP events on the
+    current stream); the prefill's rate as a fraction of the full loop's."""
+    import torch
+    import paged_kv_cache_424_amd as pa
+    src = torch.zeros(4 << 20, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    rates = {}
+    for mode in (0, 1, 2):
+        pa.pa_attention_loop_peak(src, sink, 20, mode)               # warm-up
+        best = 0.0
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            flops = pa.pa_attention_loop_peak(src, sink, iters, mode)
+            e1.record()
+            torch.cuda.synchronize()
+            best = max(best, flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+        rates[mode] = best
+    return {"tflops": rates[2], "frac_of_peak": rates[2] / PEAK_BF16_TFLOPS,
+            "prefill_over_ceiling": prefill_tflops / rates[2],
+            "mfma_and_lds_reads_only_tflops": rates[0], "with_softmax_arithmetic_tflops": rates[1],
+            "kernel": "attention_loop_kernel: per 64-key tile and wave 32 MFMA 32x32x16 bf16 with LDS fragment "
+                      "reads, 32 exp2, 16 bf16 pair conversions and row-sum steps, 32 KB tile loads per "
+                      "workgroup into double-buffered LDS, 2 workgroups per CU"}
+
+
 def measure(args, workload):
     """Time one workload's step; returns the bench line's fields (no CPU baseline)."""
     if args.partition is None:
@@ -521,6 +548,10 @@ def measure(args, workload):
                           "query_tokens": int(sum(w.chunk_len)),
                           "traffic": load_traffic(workload, "prefill"),
                           "kernel_source_hash": kernel_source_hash("prefill")}
+        # the practical ceiling of the prefill's inner loop on this chip
+        # (pa_attention_loop_peak: the same MFMA, LDS, softmax and tile-load
+        # mix per tile, with no paging), best of three launches per mode
+        res["prefill"]["loop_ceiling"] = attention_loop_ceiling(tf)
     return res, w
 
 

@@ -47,6 +47,28 @@ int pa_time_next_partitions(void* start_event, void* stop_event);
 int pa_stream_read(const void* src, size_t bytes, int32_t blocks_per_cu, int32_t unroll, int32_t blocked,
                    void* sink, void* stream);
 
+/* The practical ceiling of the prefill's inner loop: the same instructions
+ * per 64-key tile and wave as pa_prefill's loop (32 MFMA 32x32x16 bf16, each
+ * with a conflict-free 16-byte LDS fragment read, one multiply-add and one
+ * exp2, a bf16 pair conversion and a row-sum step per two) and the same tile
+ * traffic (32 KB per workgroup and tile from global memory into the idle half
+ * of a double-buffered LDS tile, a wait and a barrier), two 4-wave workgroups
+ * per compute unit, with no paging, masking or data dependence.  The
+ * yardstick beside the spec MFMA peak for pa_prefill's rate.
+ *   src:        device, 16-byte aligned, >= 2 MiB (the tile loads cycle over
+ *               its first 2 MiB; contents do not matter).
+ *   iters:      tiles per wave (>= 1).
+ *   mode:       0: MFMAs and fragment reads only; 1: plus the softmax
+ *               arithmetic; 2: plus the tile loads, wait and barrier (the
+ *               prefill's shape).
+ *   sink:       device, 4 bytes, written only in the unlikely case the result
+ *               folds to a marker value.
+ *   flops_out:  HOST int64: the MFMA flops of the launch, for rating its time.
+ * PA_ERR_INVALID_ARG for a null pointer, misalignment, src_bytes < 2 MiB,
+ * iters < 1 or mode outside 0..2.  Asynchronous on stream. */
+int pa_attention_loop_peak(const void* src, size_t src_bytes, int32_t iters, int32_t mode, void* sink,
+                           int64_t* flops_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

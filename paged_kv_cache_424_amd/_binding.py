@@ -141,6 +141,7 @@ _sig("pa_decode_append_partitions", ctypes.c_int, *_DEC_APPEND)
 _sig("pa_prefill", ctypes.c_int, _vp, _i32, _vp, _vp, _vp, _PD, _vp, _i32, _vp, _vp, _i32, _i32,
      _i32, _i32, _f32, _vp)
 _sig("pa_stream_read", ctypes.c_int, _vp, _sz, _i32, _i32, _i32, _vp, _vp)
+_sig("pa_attention_loop_peak", ctypes.c_int, _vp, _sz, _i32, _i32, _vp, _P64, _vp)
 
 
 def _check(rc, where):
@@ -467,3 +468,13 @@ def pa_stream_read(src, sink, blocks_per_cu=8, unroll=4, blocked=0, stream=None)
     _check(_lib.pa_stream_read(_dev(src, "src"), src.numel() * src.element_size(), int(blocks_per_cu),
                                int(unroll), int(blocked), _dev(sink, "sink"), _stream(stream)),
            "pa_stream_read")
+
+
+def pa_attention_loop_peak(src, sink, iters, mode=2, stream=None):
+    """The prefill inner loop's practical ceiling (see pa_measure.h); returns
+    the launch's MFMA flops."""
+    flops = ctypes.c_int64(0)
+    _check(_lib.pa_attention_loop_peak(_dev(src, "src"), src.numel() * src.element_size(), int(iters), int(mode),
+                                       _dev(sink, "sink"), ctypes.byref(flops), _stream(stream)),
+           "pa_attention_loop_peak")
+    return flops.value

@@ -1,0 +1,117 @@
+// The practical ceiling of the prefill's inner loop on this chip: a kernel
+// with the same instruction mix per 64-key tile and wave -- 32 MFMAs
+// 32x32x16 bf16, each fed a 16-byte fragment read from LDS without bank
+// conflicts, one fused multiply-add and one exp2 per MFMA, a bf16 pair
+// conversion and a row-sum step per two -- and the same tile traffic: 32 KB
+// per workgroup and tile loaded from global memory straight into the other
+// half of a double-buffered LDS tile, then a wait and a barrier.  Two
+// 4-wave workgroups per CU, as the prefill runs.  No paging, no masking, no
+// data dependence: it is the yardstick beside the 2.5 PFLOP/s spec peak for
+// the prefill's MFMA rate, as the plain streaming read is beside the 8 TB/s
+// HBM peak for the decode.  mode 0 keeps only the MFMAs and the fragment
+// reads, mode 1 adds the softmax arithmetic, mode 2 (the prefill's shape)
+// adds the tile loads.
+#include <algorithm>
+
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kLoopThreads = 256;
+constexpr int kMfmaPerTile = 32;
+constexpr size_t kLoopSrcBytes = size_t(2) << 20;       // global bytes the tile loads cycle over
+constexpr uint32_t kLoopMark = 0x9e3779b9u;
+
+// 16 bytes per lane from global memory into LDS (lane i to dst + 16 i), as
+// the prefill loads its tiles; the caller waits for vmcnt before reading.
+__device__ __forceinline__ void loop_load_to_lds(const char* src, uint16_t* dst) {
+    const uint32_t lds_addr = __builtin_amdgcn_readfirstlane(
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)dst)));
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds_addr) : "memory", "m0");
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kLoopThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attention_loop_kernel(
+    const char* __restrict__ src, int32_t iters, uint32_t* sink) {
+    __shared__ __align__(16) uint16_t sT[2][16384];          // two 32 KB tile buffers
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    for (int i = tid; i < 2 * 16384; i += kLoopThreads) (&sT[0][0])[i] = static_cast<uint16_t>(i * 7);
+    __syncthreads();
+    f32x16_t acc[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[m][e] = 0.f;
+    f32x16_t st = acc[0];
+    const u32x4 b = {static_cast<uint32_t>(lane), 1u, 2u, 3u};
+    const bf16x2_t ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+    float l = 0.f, xprev = 0.f;
+    for (int it = 0; it < iters; ++it) {
+        const int buf = it & 1;
+        if (MODE == 2) {
+            // 8 loads per wave, 32 KB per workgroup, into the buffer not being read
+            const char* base = src + ((static_cast<size_t>(blockIdx.x) * 131072 +
+                                       static_cast<size_t>(it & 63) * 32768) & (kLoopSrcBytes - 1));
+#pragma unroll
+            for (int p = 0; p < 8; ++p)
+                loop_load_to_lds(base + (w * 8 + p) * 1024 + lane * 16, &sT[buf ^ 1][(w * 8 + p) * 512]);
+        }
+#pragma unroll
+        for (int k = 0; k < kMfmaPerTile; ++k) {
+            const u32x4 f = *reinterpret_cast<const u32x4*>(&sT[buf][(lane * 8 + 512 * k) & 16383]);
+            acc[k & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f),
+                                                                  __builtin_bit_cast(bf16x8_t, b), acc[k & 3], 0, 0, 0);
+            if (MODE >= 1) {
+                const float x = __builtin_amdgcn_exp2f(fmaf(st[k & 15], 0.1f + 0.01f * k, -1.f));
+                if (k & 1) {
+                    const float2_t xx = {xprev, x};
+                    l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_convertvector(xx, bf16x2_t), ones, l, false);
+                } else {
+                    xprev = x;
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        st = acc[0] + acc[1];
+        if (MODE == 2) {
+            __builtin_amdgcn_s_waitcnt(0x0F70);               // this wave's loads have written LDS
+            __syncthreads();
+        }
+    }
+    float s = l;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s += acc[m][e];
+    if (__float_as_uint(s) == kLoopMark) sink[0] = kLoopMark;
+}
+
+}  // namespace
+}  // namespace pa
+
+extern "C" int pa_attention_loop_peak(const void* src, size_t src_bytes, int32_t iters, int32_t mode,
+                                      void* sink, int64_t* flops_out, void* stream) {
+    using namespace pa;
+    if (!src || !sink || !flops_out || src_bytes < kLoopSrcBytes || reinterpret_cast<uintptr_t>(src) % 16 ||
+        reinterpret_cast<uintptr_t>(sink) % 4 || iters < 1 || mode < 0 || mode > 2)
+        return PA_ERR_INVALID_ARG;
+    int dev = 0, cus = 0;
+    int rc = hip_status(hipGetDevice(&dev));
+    if (rc != PA_OK) return rc;
+    rc = hip_status(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+    if (rc != PA_OK) return rc;
+    const uint32_t grid = static_cast<uint32_t>(2 * cus);
+    *flops_out = static_cast<int64_t>(grid) * (kLoopThreads / 64) * iters * kMfmaPerTile * (32 * 32 * 16 * 2);
+    const auto k = mode == 0 ? attention_loop_kernel<0> : mode == 1 ? attention_loop_kernel<1>
+                                                                    : attention_loop_kernel<2>;
+    return launch_kernel(k, dim3(grid), dim3(kLoopThreads), 0, static_cast<hipStream_t>(stream),
+                         static_cast<const char*>(src), iters, static_cast<uint32_t*>(sink));
+}

@@ -486,3 +486,17 @@ def test_no_alloc_decode_rejects_beyond_its_limit_without_a_device():
     # the limit admits the mixed step's decode: 240 sequences x 64 heads x 8,192 tokens at 512
     assert pa.pa_decode_workspace_bytes(240, 64, 128, 8192, 512) <= pa.PA_DECODE_NO_ALLOC_MAX_WORKSPACE
     assert pa.pa_status_string(pa.PA_ERR_TOO_LARGE) != "unknown status"
+
+
+def test_attention_loop_peak_rejects_bad_host_arguments():
+    lib = _lib()
+    one = ctypes.c_void_p(16)
+    flops = ctypes.c_int64(0)
+    big = 2 << 20
+    f = lib.pa_attention_loop_peak
+    assert f(None, big, 10, 2, one, ctypes.byref(flops), None) == pa.PA_ERR_INVALID_ARG
+    assert f(one, big - 16, 10, 2, one, ctypes.byref(flops), None) == pa.PA_ERR_INVALID_ARG   # < 2 MiB
+    assert f(ctypes.c_void_p(24), big, 10, 2, one, ctypes.byref(flops), None) == pa.PA_ERR_INVALID_ARG
+    assert f(one, big, 0, 2, one, ctypes.byref(flops), None) == pa.PA_ERR_INVALID_ARG
+    assert f(one, big, 10, 3, one, ctypes.byref(flops), None) == pa.PA_ERR_INVALID_ARG
+    assert f(one, big, 10, 2, one, None, None) == pa.PA_ERR_INVALID_ARG
