@@ -60,7 +60,6 @@ constexpr int kKS = kD / 16;              // k-steps of the logits MFMA (16 chan
 constexpr int kMT = kD / 32;              // 32-channel tiles of the output
 constexpr int kKB = kKT / 16;             // 16-key blocks of the value MFMA
 constexpr int kMinBlock = 8;
-constexpr int kIdsPerTile = kKT / kMinBlock;   // block ids one tile can touch
 constexpr float kLazyLog2 = 8.f;          // raise the running max only when it grows by > 2^8
 constexpr int kMaxSortedChunks = 256;     // chunks ranked by length inside the kernel
 
@@ -97,11 +96,18 @@ constexpr u32x4 kZero4 = {0u, 0u, 0u, 0u};
 // wait for the load before the next LDS read of any buffer, which would
 // serialise the prefetch of tile t + 1 with the math of tile t.  The caller
 // waits for vmcnt to reach zero and then for a barrier before the data is
-// read.
+// read.  load_to_lds takes a 64-bit address per lane; load_to_lds_s a scalar
+// 64-bit base plus a 32-bit offset per lane.
 __device__ __forceinline__ void load_to_lds(const char* src, uint16_t* dst) {
     const uint32_t lds_addr = __builtin_amdgcn_readfirstlane(
         static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)dst)));
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds_addr) : "memory", "m0");
+}
+__device__ __forceinline__ void load_to_lds_s(const char* sbase, uint32_t voff, uint16_t* dst) {
+    const uint32_t lds_addr = __builtin_amdgcn_readfirstlane(
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)dst)));
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds_addr)
+                 : "memory", "m0");
 }
 constexpr bf16x2_t kOnes2 = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
 
@@ -131,7 +137,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // different bank groups.
     __shared__ __align__(16) uint16_t sK[2][kKT * kD];
     __shared__ __align__(16) uint16_t sV[2][kD * kKT];
-    __shared__ int64_t s_off[2][kIdsPerTile];   // byte offsets (id * tile bytes) of a tile's blocks
     __shared__ int s_order[kMaxSortedChunks];
 
     // ---- which (chunk, kv head, query tile) this workgroup takes ----
@@ -164,7 +169,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int pr = xcd + kNumXcds * (k / a.nqt);                      // pair in longest-first order
     const int qt = a.nqt - 1 - (k % a.nqt);
     const int g = pr % a.H;
-    const int c = nc <= kMaxSortedChunks ? s_order[pr / a.H] : pr / a.H;
+    const int c = __builtin_amdgcn_readfirstlane(nc <= kMaxSortedChunks ? s_order[pr / a.H] : pr / a.H);
     const int G = a.G;
     const int QT = kRows >> a.log2G;              // query positions per tile
 
@@ -221,22 +226,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int n_ids = bs >= kKT ? 1 : kKT / bs;
     const int nblk = (Lc + bs - 1) / bs;
     const int32_t* trow = a.tables + static_cast<int64_t>(c) * a.maxb;
-    int bad = 0;
-    // The table entry of block i of tile t (0 past the context: any valid
-    // block, masked later), and its check: an id outside the pool marks the
-    // workgroup bad and is replaced by block 0, so it is never dereferenced.
+    int bad = 0;                                  // the same in every lane
+    // The table entry of block i of tile t (clamped to the last block of the
+    // context: any valid block, masked later).
     auto block_index = [&](int t, int i) { return (t * kKT) / bs + i; };
     auto raw_block_id = [&](int b) { return trow[min(b, nblk - 1)]; };   // nblk >= 1
-    auto checked = [&](int b, int id) -> int {    // branch-free
-        const bool inside = b < nblk;
-        const bool ok = id >= 0 && id < a.N;
-        bad |= (inside && !ok) ? 1 : 0;
-        return inside && ok ? id : 0;
-    };
-    auto block_id = [&](int t, int i) -> int {
-        const int b = block_index(t, i);
-        return checked(b, raw_block_id(b));
-    };
 
     // ---- tile loader: global -> LDS directly (no registers), 16 bytes per lane ----
     // Such a load writes its wave's 64 segments to 64 consecutive LDS
@@ -255,37 +249,67 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int64_t tile_bytes = static_cast<int64_t>(a.H) * bs * kD * 2;
     const char* kbase = reinterpret_cast<const char*>(a.kc) + static_cast<int64_t>(g) * bs * kD * 2;
     const char* vbase = reinterpret_cast<const char*>(a.vc) + static_cast<int64_t>(g) * kD * bs * 2;
-    int kslot[4], koff[4], vslot[4], voff[4];
+    int kslot[4];                    // block slot of K load p: the same for the whole wave
+    int koff[4], vslot[4], voff[4];  // per lane
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const int key = 16 * w + 4 * p + (lane >> 4);
         const int seg = (lane & 15) ^ (key & 15);              // channels 8 seg .. +7
-        kslot[p] = big_blocks ? 0 : key >> log2bs;
+        kslot[p] = big_blocks ? 0 : (16 * w + 4 * p) >> log2bs;
         koff[p] = (((seg >> 2) * bs + (big_blocks ? key : key & (bs - 1))) * 32 + (seg & 3) * 8) * 2;
         const int d = 32 * w + 8 * p + (lane >> 3);
         const int vkey = 8 * ((lane & 7) ^ ((d >> 1) & 7));    // keys vkey .. +7
         vslot[p] = big_blocks ? 0 : vkey >> log2bs;
         voff[p] = (d * bs + (big_blocks ? vkey : vkey & (bs - 1))) * 2;
     }
-    // offs: the byte offsets of the tile's blocks, kept in LDS so that no
-    // thread multiplies a block id by the block's size
-    auto load_tile = [&](int t, const int64_t* offs, int buf) {
+    // A tile's block ids are read two tiles ahead, lane i taking id i (a
+    // vector load, waited for with the tile's own loads; lanes past n_ids
+    // repeat the last one), and checked per lane: an id outside the pool
+    // marks the workgroup bad and is replaced by block 0, so it is never
+    // dereferenced.  A K load instruction reads one block, so its id is
+    // taken from its lane into a scalar register and the load's address is
+    // that block plus a fixed per-lane offset; a V load instruction spans the
+    // tile's blocks, so each lane fetches the id it needs from the lane that
+    // holds it.
+    auto load_raw = [&](int t) { return raw_block_id(block_index(t, min(lane, n_ids - 1))); };
+    auto check_ids = [&](int t, int raw) {
+        const int b = block_index(t, min(lane, n_ids - 1));
+        const bool inside = b < nblk;
+        const bool ok = raw >= 0 && raw < a.N;
+        if (__builtin_amdgcn_ballot_w64(inside && !ok)) bad = 1;
+        return inside && ok ? raw : 0;
+    };
+    struct TileIds {
+        int k[4];   // uniform
+        int v[4];   // per lane
+    };
+    auto tile_ids = [&](int ids, TileIds& T) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) T.k[p] = __builtin_amdgcn_readlane(ids, kslot[p]);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) T.v[p] = __builtin_amdgcn_ds_bpermute(vslot[p] << 2, ids);
+    };
+    // Addresses of tile t's eight loads: K load p reads from ksb[p] + koff[p]
+    // (a scalar base), V load p from va[p].
+    struct TileAddr {
+        const char* ksb[4];
+        const char* va[4];
+    };
+    auto tile_addr = [&](int t, const TileIds& T, TileAddr& A) {
         // the tile's offset inside its block (only for blocks larger than a tile)
         const int in_blk = big_blocks ? ((t * kKT) & (bs - 1)) : 0;
-        // all eight block offsets are read before the first load: each load is
-        // an asm statement that orders memory, so a read placed after one would
-        // wait for it and the reads' latencies would add up
-        int64_t ok[4], ov[4];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) ok[p] = offs[kslot[p]];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) ov[p] = offs[vslot[p]];
+        for (int p = 0; p < 4; ++p) A.ksb[p] = kbase + static_cast<int64_t>(T.k[p]) * tile_bytes + in_blk * 32 * 2;
 #pragma unroll
         for (int p = 0; p < 4; ++p)
-            load_to_lds(kbase + ok[p] + koff[p] + in_blk * 32 * 2, &sK[buf][(16 * w + 4 * p) * kD]);
-#pragma unroll
-        for (int p = 0; p < 4; ++p)
-            load_to_lds(vbase + ov[p] + voff[p] + in_blk * 2, &sV[buf][(32 * w + 8 * p) * kKT]);
+            A.va[p] = vbase + static_cast<uint64_t>(static_cast<uint32_t>(T.v[p])) * tile_bytes + voff[p] + in_blk * 2;
+    };
+    // load i of 8 (K loads 0-3, then V loads 0-3) into buffer buf
+    auto load_part = [&](const TileAddr& A, int i, int buf) {
+        if (i < 4)
+            load_to_lds_s(A.ksb[i], koff[i], &sK[buf][(16 * w + 4 * i) * kD]);
+        else
+            load_to_lds(A.va[i - 4], &sV[buf][(32 * w + 8 * (i - 4)) * kKT]);
     };
     f32x16_t acc[kMT];
 #pragma unroll
@@ -317,12 +341,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     };
 
     // ---- prologue: ids of tiles 0 and 1, then tile 0 into LDS ----
-    if (tid < n_ids) {
-        s_off[0][tid] = block_id(0, tid) * tile_bytes;
-        if (nkt > 1) s_off[1][tid] = block_id(1, tid) * tile_bytes;
+    TileIds T;                                    // ids of the next tile to load
+    {
+        const int r0 = load_raw(0);
+        const int r1 = load_raw(min(1, nkt - 1));
+        tile_ids(check_ids(0, r0), T);
+        TileAddr A;
+        tile_addr(0, T, A);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) load_part(A, i, 0);
+        tile_ids(check_ids(min(1, nkt - 1), r1), T);
     }
-    __syncthreads();
-    load_tile(0, s_off[0], 0);
     wait_loads();
     if (nkt == 1) zero_v_tail(0, 0);
     __syncthreads();
@@ -330,15 +359,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int kt = 0; kt < nkt; ++kt) {
         const int buf = kt & 1;
         const int base = kt * kKT;
-        if (kt + 1 < nkt) load_tile(kt + 1, s_off[buf ^ 1], buf ^ 1);
-        // tile kt + 2's block ids: loaded now, checked and stored after this
-        // tile's math, so the wait for them is not on the critical path
+        // Tile kt + 1's eight loads are issued one per channel step of the
+        // logits below: issued back to back, the four waves' loads queued
+        // behind each other in the memory pipeline and each wave waited
+        // there instead of issuing matrix instructions.  In the last
+        // iteration they fetch tile nkt - 1 again into the free buffer, so no
+        // load sits behind a branch.
+        TileAddr A;
+        tile_addr(min(kt + 1, nkt - 1), T, A);
+        // tile kt + 2's block ids: loaded now, checked after this tile's
+        // math, so the wait for them is not on the critical path
         // Every thread loads and checks one id in every iteration (lanes
         // past n_ids, and iterations with no tile kt + 2, repeat an id
         // already read), so the load is always consumed on the same path.
-        const bool next_ids = kt + 2 < nkt;
-        const int nb_idx = block_index(min(kt + 2, nkt - 1), min(tid, n_ids - 1));
-        const int nid = raw_block_id(nb_idx);
+        const int t2 = min(kt + 2, nkt - 1);
+        const int raw = load_raw(t2);
 
         // ---- logits S^T[key][row] for the tile's two 32-key MFMA tiles ----
         // The two 32-key MFMA chains are interleaved (channel step outer), so
@@ -350,13 +385,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
             for (int e = 0; e < 16; ++e) st[t][e] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < kKS; ++ks)
+        for (int ks = 0; ks < kKS; ++ks) {
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 const uint16_t* krow = &sK[buf][(32 * t + krow0) * kD];
                 const u32x4 kf = *reinterpret_cast<const u32x4*>(krow + 8 * ((2 * ks + hh) ^ kx));
                 st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[ks]), st[t], 0, 0, 0);
             }
+            load_part(A, ks, buf ^ 1);
+        }
         // Scheduling hint (LDS reads = 0x100, MFMA = 0x008): 4 fragment reads,
         // then (2 MFMAs, 2 reads) x 6, then 4 MFMAs, so each read leads its MFMA
         // by two MFMA pairs instead of one.
@@ -428,8 +465,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         // the scheduler cannot hoist it (and the wait with it) into the value
         // products above.
         __builtin_amdgcn_sched_barrier(0);
-        const int id = checked(nb_idx, nid);
-        if (next_ids && tid < n_ids) s_off[buf][tid] = id * tile_bytes;
+        tile_ids(check_ids(t2, raw), T);
         if (kt + 2 == nkt) zero_v_tail(buf ^ 1, kt + 1);
         __syncthreads();
     }
