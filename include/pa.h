@@ -409,7 +409,8 @@ int pa_decode_no_alloc(void* out, int32_t out_dtype, const void* q, const void* 
  * outside [0, num_blocks) are set to NaN (when they lie inside the output), and
  * nothing is read out of bounds.  Supported: bf16 cache, head_dim 128,
  * num_q_heads/num_kv_heads a power of two up to 16, block_size 8..256 a power
- * of two.  scale must be finite and > 0 (PA_ERR_INVALID_ARG otherwise): the
+ * of two, one block of all kv heads (num_kv_heads x block_size x 256 bytes)
+ * below 4 GiB.  scale must be finite and > 0 (PA_ERR_INVALID_ARG otherwise): the
  * running maximum is kept on the unscaled logits.  The value pass takes the
  * softmax weights in bf16 (fp32 accumulate), and each row's weight sum is taken
  * from the same bf16 weights. */

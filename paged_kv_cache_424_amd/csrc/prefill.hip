@@ -38,6 +38,8 @@
 
 #include <cmath>
 
+#include <type_traits>
+
 #include "pa_internal.h"
 
 namespace pa {
@@ -48,6 +50,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -96,18 +99,19 @@ constexpr u32x4 kZero4 = {0u, 0u, 0u, 0u};
 // wait for the load before the next LDS read of any buffer, which would
 // serialise the prefetch of tile t + 1 with the math of tile t.  The caller
 // waits for vmcnt to reach zero and then for a barrier before the data is
-// read.  load_to_lds takes a 64-bit address per lane; load_to_lds_s a scalar
-// 64-bit base plus a 32-bit offset per lane.
-__device__ __forceinline__ void load_to_lds(const char* src, uint16_t* dst) {
-    const uint32_t lds_addr = __builtin_amdgcn_readfirstlane(
-        static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)dst)));
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds_addr) : "memory", "m0");
+// read.  m0v is the LDS byte address of the wave's destination.
+// load_to_lds takes a 64-bit address per lane; load_to_lds_s a scalar 64-bit
+// base plus a 32-bit offset per lane.
+__device__ __forceinline__ void load_to_lds(const char* src, uint32_t m0v) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(m0v) : "memory", "m0");
 }
-__device__ __forceinline__ void load_to_lds_s(const char* sbase, uint32_t voff, uint16_t* dst) {
-    const uint32_t lds_addr = __builtin_amdgcn_readfirstlane(
-        static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)dst)));
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds_addr)
+__device__ __forceinline__ void load_to_lds_s(const char* sbase, uint32_t voff, uint32_t m0v) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(m0v)
                  : "memory", "m0");
+}
+// LDS byte address of a shared-memory location (the same for every lane)
+__device__ __forceinline__ uint32_t lds_address(const uint16_t* p) {
+    return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)p)));
 }
 constexpr bf16x2_t kOnes2 = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
 
@@ -295,21 +299,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const char* ksb[4];
         const char* va[4];
     };
+    // Block offsets are ids times the block's bytes, 32 x 32 -> 64 bits (the
+    // host checks that the bytes fit 32 bits); V load p's per-lane base is
+    // fixed.
+    const uint32_t tb32 = static_cast<uint32_t>(tile_bytes);
+    const char* vb0[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) vb0[p] = vbase + voff[p];
     auto tile_addr = [&](int t, const TileIds& T, TileAddr& A) {
         // the tile's offset inside its block (only for blocks larger than a tile)
         const int in_blk = big_blocks ? ((t * kKT) & (bs - 1)) : 0;
 #pragma unroll
-        for (int p = 0; p < 4; ++p) A.ksb[p] = kbase + static_cast<int64_t>(T.k[p]) * tile_bytes + in_blk * 32 * 2;
+        for (int p = 0; p < 4; ++p)
+            A.ksb[p] = kbase + static_cast<uint64_t>(static_cast<uint32_t>(T.k[p])) * tb32 + in_blk * 32 * 2;
 #pragma unroll
         for (int p = 0; p < 4; ++p)
-            A.va[p] = vbase + static_cast<uint64_t>(static_cast<uint32_t>(T.v[p])) * tile_bytes + voff[p] + in_blk * 2;
+            A.va[p] = vb0[p] + static_cast<uint64_t>(static_cast<uint32_t>(T.v[p])) * tb32 + in_blk * 2;
     };
+    // LDS destinations of this wave's loads in buffer 0 (buffer 1 is one
+    // tile on), computed once: worked out per load, the compiler kept these
+    // uniform addresses in vector registers.
+    const uint32_t m0k = lds_address(&sK[0][16 * w * kD]);
+    const uint32_t m0v = lds_address(&sV[0][32 * w * kKT]);
     // load i of 8 (K loads 0-3, then V loads 0-3) into buffer buf
     auto load_part = [&](const TileAddr& A, int i, int buf) {
         if (i < 4)
-            load_to_lds_s(A.ksb[i], koff[i], &sK[buf][(16 * w + 4 * i) * kD]);
+            load_to_lds_s(A.ksb[i], koff[i], m0k + (buf * kKT * kD + 4 * i * kD) * 2);
         else
-            load_to_lds(A.va[i - 4], &sV[buf][(32 * w + 8 * (i - 4)) * kKT]);
+            load_to_lds(A.va[i - 4], m0v + (buf * kD * kKT + 8 * (i - 4) * kKT) * 2);
     };
     f32x16_t acc[kMT];
 #pragma unroll
@@ -356,8 +373,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     if (nkt == 1) zero_v_tail(0, 0);
     __syncthreads();
 
-    for (int kt = 0; kt < nkt; ++kt) {
-        const int buf = kt & 1;
+    // Fragment addresses in buffer 0: K fragment of channel step ks (rows of
+    // the first 32-key half; the second is 32 rows on), V fragment of key
+    // segment group (t, kb) (channel tile 0; tile mt is 32 rows on).  The
+    // tile loop is unrolled by two, so the buffer is a constant and every
+    // fragment read is one of these addresses plus an immediate offset.
+    const uint16_t* kfp[kKS];
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) kfp[ks] = &sK[0][krow0 * kD + 8 * ((2 * ks + hh) ^ kx)];
+    const uint16_t* vfp[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) vfp[t][kb] = &sV[0][col * kKT + 8 * ((hh + 4 * t + 2 * kb) ^ vx)];
+
+    // One key tile kt, read from buffer BUF = kt & 1.
+    auto tile = [&](int kt, auto buf_c) {
+        constexpr int buf = decltype(buf_c)::value;
         const int base = kt * kKT;
         // Tile kt + 1's eight loads are issued one per channel step of the
         // logits below: issued back to back, the four waves' loads queued
@@ -388,8 +420,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         for (int ks = 0; ks < kKS; ++ks) {
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const uint16_t* krow = &sK[buf][(32 * t + krow0) * kD];
-                const u32x4 kf = *reinterpret_cast<const u32x4*>(krow + 8 * ((2 * ks + hh) ^ kx));
+                const u32x4 kf = *reinterpret_cast<const u32x4*>(kfp[ks] + buf * kKT * kD + 32 * t * kD);
                 st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[ks]), st[t], 0, 0, 0);
             }
             load_part(A, ks, buf ^ 1);
@@ -436,25 +467,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         // so the two overlap within the wave.
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            bf16x8_t pb[2];
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                pb[e >> 3][e & 7] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(st[t][e], cscale, neg_m)));
-            // the row sum takes the same bf16 weights as the value product,
-            // two per instruction
+            // weights converted to bf16 in pairs (one conversion per two); the
+            // row sum takes the same bf16 weights as the value product, two
+            // per instruction
+            u32x4 pw[2];
 #pragma unroll
             for (int e = 0; e < 16; e += 2) {
-                const bf16x2_t w2 = {pb[e >> 3][e & 7], pb[e >> 3][(e & 7) + 1]};
+                const float2_t x = {__builtin_amdgcn_exp2f(fmaf(st[t][e], cscale, neg_m)),
+                                    __builtin_amdgcn_exp2f(fmaf(st[t][e + 1], cscale, neg_m))};
+                const bf16x2_t w2 = __builtin_convertvector(x, bf16x2_t);
+                pw[e >> 3][(e & 7) >> 1] = __builtin_bit_cast(uint32_t, w2);
                 l_run = __builtin_amdgcn_fdot2_f32_bf16(w2, kOnes2, l_run, false);
             }
+            const bf16x8_t pb[2] = {as_bf16x8(pw[0]), as_bf16x8(pw[1])};
             // ---- values: O^T[channel][row] += V^T[channel][key] . P^T[key][row] ----
 #pragma unroll
             for (int mt = 0; mt < kMT; ++mt) {
-                const uint16_t* vrow = &sV[buf][(32 * mt + col) * kKT];
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
-                    const int sgl = hh + 4 * t + 2 * kb;           // keys base + 8 sgl .. +7
-                    const u32x4 vf = *reinterpret_cast<const u32x4*>(vrow + 8 * (sgl ^ vx));
+                    // keys base + 8 (hh + 4 t + 2 kb) .. +7 of channel 32 mt + col
+                    const u32x4 vf =
+                        *reinterpret_cast<const u32x4*>(vfp[t][kb] + buf * kD * kKT + 32 * mt * kKT);
                     acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), pb[kb], acc[mt], 0, 0, 0);
                 }
             }
@@ -468,6 +501,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         tile_ids(check_ids(t2, raw), T);
         if (kt + 2 == nkt) zero_v_tail(buf ^ 1, kt + 1);
         __syncthreads();
+    };
+    for (int kt = 0; kt < nkt; kt += 2) {
+        tile(kt, std::integral_constant<int, 0>{});
+        if (kt + 1 < nkt) tile(kt + 1, std::integral_constant<int, 1>{});
     }
     bad = __syncthreads_or(bad);
 
@@ -516,6 +553,9 @@ extern "C" int pa_prefill(void* out, int32_t out_dtype, const void* q, const voi
     if (desc->kv_dtype != PA_BF16 || desc->head_dim != kD) return PA_ERR_UNSUPPORTED;
     if (!is_pow2(G) || G > 16) return PA_ERR_UNSUPPORTED;
     if (!is_pow2(desc->block_size) || desc->block_size < kMinBlock || desc->block_size > 256)
+        return PA_ERR_UNSUPPORTED;
+    // one block of all kv heads (the stride between blocks) must fit 32 bits
+    if (static_cast<int64_t>(H) * desc->block_size * kD * 2 > static_cast<int64_t>(UINT32_MAX))
         return PA_ERR_UNSUPPORTED;
     if (num_chunks == 0 || max_query_len == 0 || num_query_tokens == 0) return PA_OK;
     if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start_loc)
