@@ -265,8 +265,9 @@ def attention_loop_ceiling(prefill_tflops, iters=1000, reps=3):
             "prefill_over_ceiling": prefill_tflops / rates[2],
             "mfma_and_lds_reads_only_tflops": rates[0], "with_softmax_arithmetic_tflops": rates[1],
             "kernel": "attention_loop_kernel: per 64-key tile and wave 32 MFMA 32x32x16 bf16 with LDS fragment "
-                      "reads, 32 exp2, 16 bf16 pair conversions and row-sum steps, 32 KB tile loads per "
-                      "workgroup into double-buffered LDS, 2 workgroups per CU"}
+                      "reads, 32 exp2, 16 bf16 pair conversions and row-sum steps (each exponential consumed "
+                      "four steps later, four row-sum accumulators), 32 KB tile loads per workgroup into "
+                      "double-buffered LDS (one load per four MFMAs), 2 workgroups per CU"}
 
 
 def measure(args, workload):

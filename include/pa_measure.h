@@ -52,9 +52,12 @@ int pa_stream_read(const void* src, size_t bytes, int32_t blocks_per_cu, int32_t
  * with a conflict-free 16-byte LDS fragment read, one multiply-add and one
  * exp2, a bf16 pair conversion and a row-sum step per two) and the same tile
  * traffic (32 KB per workgroup and tile from global memory into the idle half
- * of a double-buffered LDS tile, a wait and a barrier), two 4-wave workgroups
- * per compute unit, with no paging, masking or data dependence.  The
- * yardstick beside the spec MFMA peak for pa_prefill's rate.
+ * of a double-buffered LDS tile, one load per four MFMAs, a wait and a
+ * barrier), two 4-wave workgroups per compute unit, with no paging or
+ * masking, and the vector work free of the MFMAs' results (each exponential
+ * is consumed four steps later, the row sums go to four accumulators) so
+ * that the hardware overlaps the two as far as it can.  The yardstick beside
+ * the spec MFMA peak for pa_prefill's rate.
  *   src:        device, 16-byte aligned, >= 2 MiB (the tile loads cycle over
  *               its first 2 MiB; contents do not matter).
  *   iters:      tiles per wave (>= 1).

@@ -4,13 +4,16 @@
 // conflicts, one fused multiply-add and one exp2 per MFMA, a bf16 pair
 // conversion and a row-sum step per two -- and the same tile traffic: 32 KB
 // per workgroup and tile loaded from global memory straight into the other
-// half of a double-buffered LDS tile, then a wait and a barrier.  Two
-// 4-wave workgroups per CU, as the prefill runs.  No paging, no masking, no
-// data dependence: it is the yardstick beside the 2.5 PFLOP/s spec peak for
-// the prefill's MFMA rate, as the plain streaming read is beside the 8 TB/s
-// HBM peak for the decode.  mode 0 keeps only the MFMAs and the fragment
-// reads, mode 1 adds the softmax arithmetic, mode 2 (the prefill's shape)
-// adds the tile loads.
+// half of a double-buffered LDS tile, one load per four MFMAs, then a wait
+// and a barrier.  Two 4-wave workgroups per CU, as the prefill runs.  No
+// paging, no masking, and no dependence of the softmax work on the MFMAs:
+// each exponential's result is consumed four steps later and the row sums
+// go to four independent accumulators, so the hardware may overlap the
+// vector work with the matrix work as far as it can.  It is the yardstick
+// beside the 2.5 PFLOP/s spec peak for the prefill's MFMA rate, as the
+// plain streaming read is beside the 8 TB/s HBM peak for the decode.  mode
+// 0 keeps only the MFMAs and the fragment reads, mode 1 adds the softmax
+// arithmetic, mode 2 (the prefill's shape) adds the tile loads.
 #include <algorithm>
 
 #include "pa_internal.h"
@@ -53,32 +56,41 @@ __global__ __launch_bounds__(kLoopThreads) __attribute__((amdgpu_waves_per_eu(2,
     f32x16_t st = acc[0];
     const u32x4 b = {static_cast<uint32_t>(lane), 1u, 2u, 3u};
     const bf16x2_t ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
-    float l = 0.f, xprev = 0.f;
+    float l[4] = {0.f, 0.f, 0.f, 0.f};
+    float xs[8];                                              // exponentials of the last eight steps
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xs[i] = 0.f;
     for (int it = 0; it < iters; ++it) {
         const int buf = it & 1;
-        if (MODE == 2) {
-            // 8 loads per wave, 32 KB per workgroup, into the buffer not being read
-            const char* base = src + ((static_cast<size_t>(blockIdx.x) * 131072 +
-                                       static_cast<size_t>(it & 63) * 32768) & (kLoopSrcBytes - 1));
-#pragma unroll
-            for (int p = 0; p < 8; ++p)
-                loop_load_to_lds(base + (w * 8 + p) * 1024 + lane * 16, &sT[buf ^ 1][(w * 8 + p) * 512]);
-        }
+        // 8 loads per wave, 32 KB per workgroup, into the buffer not being read
+        const char* base = src + ((static_cast<size_t>(blockIdx.x) * 131072 +
+                                   static_cast<size_t>(it & 63) * 32768) & (kLoopSrcBytes - 1));
 #pragma unroll
         for (int k = 0; k < kMfmaPerTile; ++k) {
             const u32x4 f = *reinterpret_cast<const u32x4*>(&sT[buf][(lane * 8 + 512 * k) & 16383]);
             acc[k & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f),
                                                                   __builtin_bit_cast(bf16x8_t, b), acc[k & 3], 0, 0, 0);
             if (MODE >= 1) {
-                const float x = __builtin_amdgcn_exp2f(fmaf(st[k & 15], 0.1f + 0.01f * k, -1.f));
-                if (k & 1) {
-                    const float2_t xx = {xprev, x};
-                    l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_convertvector(xx, bf16x2_t), ones, l, false);
-                } else {
-                    xprev = x;
+                xs[k & 7] = __builtin_amdgcn_exp2f(fmaf(st[k & 15], 0.1f + 0.01f * k, -1.f));
+                if ((k & 1) && k >= 5) {                      // the pair of steps k - 5, k - 4
+                    const float2_t xx = {xs[(k - 5) & 7], xs[(k - 4) & 7]};
+                    l[(k >> 1) & 3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_convertvector(xx, bf16x2_t), ones,
+                                                                      l[(k >> 1) & 3], false);
                 }
             }
-            __builtin_amdgcn_sched_barrier(0);
+            if (MODE == 2 && (k & 3) == 3) {
+                const int p = k >> 2;
+                loop_load_to_lds(base + (w * 8 + p) * 1024 + lane * 16, &sT[buf ^ 1][(w * 8 + p) * 512]);
+            }
+        }
+        if (MODE >= 1) {
+            // the tile's last two pairs
+#pragma unroll
+            for (int k = 33; k < 37; k += 2) {
+                const float2_t xx = {xs[(k - 5) & 7], xs[(k - 4) & 7]};
+                l[(k >> 1) & 3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_convertvector(xx, bf16x2_t), ones,
+                                                                  l[(k >> 1) & 3], false);
+            }
         }
         st = acc[0] + acc[1];
         if (MODE == 2) {
@@ -86,7 +98,7 @@ __global__ __launch_bounds__(kLoopThreads) __attribute__((amdgpu_waves_per_eu(2,
             __syncthreads();
         }
     }
-    float s = l;
+    float s = l[0] + l[1] + l[2] + l[3];
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
