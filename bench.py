@@ -8,12 +8,15 @@ resident in HBM:
 2. the cache write of the tokens the step appends; when those are only each
    decode sequence's newest token, the decode kernel stores them itself
    instead (pa_decode_append; --append on/off overrides);
-3. the split-K decode partition kernel, then the rescaling reduce;
-4. for the mixed continuous-batching workload, the prefill-chunk kernel, after
-   the decode (--overlap on runs it on a second stream beside the decode;
-   both wait for the cache write).
+3. for the mixed continuous-batching workload, the prefill-chunk kernel
+   (--overlap on runs it on a second stream beside the decode instead; both
+   wait for the cache write);
+4. the split-K decode partition kernel, then the rescaling reduce.
 
-Prints one JSON line.
+Prints one JSON line.  Warm-up runs the W untimed steps and then more, until
+--warmup-ms (default 150) of wall time has passed: the GPU lowers its clocks
+while the host builds the workload, and the first 20-40 steps after that run
+10-20 % slow.  The line records how many warm-up steps ran.
 
     python bench.py [--steps K] [--warmup W] [--workload c2|c3|c4|c4p|c5]
     python bench.py --study prefix-cache|fragmentation|block-size|batch1|stream-peak
@@ -23,9 +26,9 @@ the largest configuration that fits one GPU.
 - 240 decode sequences, lognormal context lengths (median 1024, [64, 8192]),
   plus 16 prefill chunks of 256 queries over contexts U{256..4096}.
 - 64 query / 8 KV heads, head_dim 128, bf16 cache in 32-token blocks.
-- The step writes the chunks' and the decode tokens' K/V, decodes with the
-  balanced split (--partition P selects P-token partitions), then runs the
-  causal prefill chunks.
+- The step writes the chunks' and the decode tokens' K/V, runs the causal
+  prefill chunks, then decodes with the balanced split (--partition P selects
+  P-token partitions).
 The line carries the decode kernel's HBM roofline (`roofline`), the prefill
 kernel's MFMA roofline (`prefill`), and, timed the same way after the mixed
 step in the same run, the long-context decode of 8 x 32,768 tokens in its
@@ -356,12 +359,13 @@ def measure(args, workload):
     overlap = pre is not None and args.overlap == "on"
     side = torch.cuda.Stream() if overlap else None
 
-    # Events: in the timed steps only around the partition kernel (2, 3) and
+    # Events: in the timed steps only around the partition kernel (7, 3) and
     # the prefill kernel (5, 6), so that event records add no gaps elsewhere;
     # a separate pass after the timed region records all of them: 0 start,
-    # 1 after copy_blocks, 2 after cache_write, 3 after the partition kernel,
-    # 4 after the reduce, 5 before and 6 after prefill (on the prefill's stream).
-    timed_marks = (2, 3, 5, 6) if pre is not None else (2, 3)
+    # 1 after copy_blocks, 2 after cache_write, 7 before and 3 after the
+    # partition kernel, 4 after the reduce, 5 before and 6 after prefill (on
+    # the prefill's stream).
+    timed_marks = (7, 3, 5, 6) if pre is not None else (7, 3)
 
     def step(i, ev=None, marks=timed_marks, dispatch_ev=None, use_side=None):
         use_side = overlap if use_side is None else use_side
@@ -390,13 +394,18 @@ def measure(args, workload):
                 prefill()
                 joined = torch.cuda.Event()
                 joined.record()
-        decode(kc, vc, mark, dispatch_ev)
+        # On one stream the prefill runs before the decode: both need only the
+        # cache write, and the decode then streams HBM after the compute-bound
+        # prefill rather than straight after the cache write (measured on the
+        # mixed step: decode 288 vs 291-299 us, step 581 vs 585-594 us).
         if pre is not None and not use_side:
             prefill()
+        decode(kc, vc, mark, dispatch_ev)
         if joined is not None:
             main.wait_event(joined)
 
     def decode(kc, vc, mark, dispatch_ev):
+        mark(7)
         if dispatch_ev is not None:
             pa.pa_time_next_partitions(*dispatch_ev)
         if newest is not None:
@@ -409,17 +418,28 @@ def measure(args, workload):
         pa.pa_decode_reduce(out, st.lens, Hq, D, max_ctx, args.partition, ws)
         mark(4)
 
-    for i in range(args.warmup):
-        step(i)
+    # Warm-up: W steps, and more until --warmup-ms of wall time has passed.
+    # The GPU lowers its clocks while the host builds the workload; measured,
+    # the first 20-40 steps after a 2 s idle ran 10-20 % slow (prefill 307 ->
+    # 258 us, decode 316 -> 280 us) and later steps held steady.  Every
+    # warm-up and timed step is the whole step.
+    t_w = time.perf_counter()
+    n_warm = 0
+    while n_warm < args.warmup or (time.perf_counter() - t_w) * 1e3 < args.warmup_ms:
+        step(n_warm)
+        n_warm += 1
+        if n_warm % 8 == 0:
+            torch.cuda.synchronize()          # keep the host clock in step with the GPU
     torch.cuda.synchronize()
-    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(7)) for _ in range(args.steps)]
+    warm_ms = (time.perf_counter() - t_w) * 1e3
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(8)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        step(n_warm + i, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    part_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    part_ms = [e[7].elapsed_time(e[3]) for e in evs]
     part_avg_s = float(np.mean(part_ms)) / 1e3
 
     # the partition kernel's dispatch events (recorded once here so that their
@@ -430,7 +450,7 @@ def measure(args, workload):
             e.record()
     torch.cuda.synchronize()
     for i in range(args.steps):
-        step(args.warmup + i, dispatch_ev=evd[i])
+        step(n_warm + i, dispatch_ev=evd[i])
     torch.cuda.synchronize()
     dispatch_ms = [e[0].elapsed_time(e[1]) for e in evd]
     assert torch.isfinite(out).all()
@@ -443,14 +463,14 @@ def measure(args, workload):
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         for i in range(args.steps):
-            step(args.warmup + i, use_side=False)
+            step(n_warm + i, use_side=False)
         torch.cuda.synchronize()
         serial_ms = (time.perf_counter() - t1) * 1e3 / args.steps
 
     # per-kernel times, all events recorded (not part of the timed region)
-    evk = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(7)) for _ in range(args.steps)]
+    evk = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(8)) for _ in range(args.steps)]
     for i in range(args.steps):
-        step(args.warmup + i, evk[i], marks=(0, 1, 2, 3, 4, 5, 6), use_side=False)
+        step(n_warm + i, evk[i], marks=(0, 1, 2, 3, 4, 5, 6, 7), use_side=False)
     torch.cuda.synchronize()
 
     def avg_us(a, b):
@@ -489,6 +509,8 @@ def measure(args, workload):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": n_warm,
+        "warmup_ms": warm_ms,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -500,9 +522,9 @@ def measure(args, workload):
                    "block_size": w.block_size, "partition": args.partition, "pool_copies": copies,
                    "step": ("copy_blocks + " if pairs else "") +
                            ("cache_write + " if slots.numel() else "") +
+                           ("prefill + " if pre is not None and not overlap else "") +
                            ("decode_append_partitions" if newest is not None else "decode_partitions") +
-                           " + decode_reduce" + ((" || prefill (second stream)" if overlap else " + prefill")
-                                                 if pre is not None else "")},
+                           " + decode_reduce" + (" || prefill (second stream)" if overlap else "")},
         "roofline": {"bound": "hbm", "kernel": "decode_partition_kernel", "achieved": achieved,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                      "traffic": load_traffic(workload), "algorithmic_bytes_per_launch": algo,
@@ -519,7 +541,7 @@ def measure(args, workload):
         "ms_per_step_one_stream": serial_ms,
         "kernels_us_untimed_pass": {"copy_blocks": avg_us(0, 1) if pairs else None,
                                     "cache_write": avg_us(1, 2) if slots.numel() else None,
-                       "decode_partitions": avg_us(2, 3), "decode_reduce": avg_us(3, 4),
+                       "decode_partitions": avg_us(7, 3), "decode_reduce": avg_us(3, 4),
                        "prefill": avg_us(5, 6) if pre is not None else None},
     }
     # the practical read rate for the same byte count: a plain streaming read
@@ -561,6 +583,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup-ms", type=float, default=150.0,
+                    help="after the W warm-up steps, keep running untimed whole steps until this much "
+                         "wall time has passed (the GPU lowers its clocks while idle; the first tens of "
+                         "steps after the host-side setup run 10-20 %% slow)")
     ap.add_argument("--workload", default="c5", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--no-extra", action="store_true",
                     help="with the mixed step (c5), skip the long-context decode (c3) that the "
