@@ -32,9 +32,9 @@
 // (8-bit mantissa, fp32 accumulation).  The running maximum is raised lazily:
 // only when a tile's maximum exceeds it by more than 2^8 in weight, so the
 // accumulator is rescaled a few times per row rather than per tile; weights
-// stay below 2^8, exact in the fp32 sums.  LDS rows are padded (K rows by
-// 16 bytes, V rows by 16 bytes) so that each quarter-wave's 16-byte reads hit
-// 16 different bank groups.
+// stay below 2^8, exact in the fp32 sums.  The LDS tiles are XOR-swizzled
+// (see the kernel's shared arrays) so that each quarter-wave's 16-byte reads
+// hit 16 different bank groups.
 
 #include <cmath>
 
@@ -142,6 +142,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     __shared__ __align__(16) uint16_t sK[2][kKT * kD];
     __shared__ __align__(16) uint16_t sV[2][kD * kKT];
     __shared__ int s_order[kMaxSortedChunks];
+    __shared__ int s_clen[kMaxSortedChunks];       // context length of every chunk
+    __shared__ int s_qsl[kMaxSortedChunks + 1];    // query start of every chunk, and the end
 
     // ---- which (chunk, kv head, query tile) this workgroup takes ----
     // Workgroup b runs on XCD b % 8 (dispatch is round robin over the XCDs).
@@ -153,12 +155,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // chunks), query tiles of a chunk from the last one down.
     const int tid = threadIdx.x;
     const int nc = a.num_chunks;
-    if (nc <= kMaxSortedChunks) {
+    const bool few = nc <= kMaxSortedChunks;
+    if (few) {
+        // every chunk's length and query start read once, in parallel, then
+        // ranked from LDS
+        for (int i = tid; i <= nc; i += kThreads) {
+            if (i < nc) s_clen[i] = a.lens[i];
+            s_qsl[i] = a.qsl[i];
+        }
+        __syncthreads();
         for (int i = tid; i < nc; i += kThreads) {
-            const int Li = a.lens[i];
+            const int Li = s_clen[i];
             int rank = 0;
             for (int jc = 0; jc < nc; ++jc) {
-                const int Lj = a.lens[jc];
+                const int Lj = s_clen[jc];
                 rank += (Lj > Li) || (Lj == Li && jc < i);
             }
             s_order[rank] = i;
@@ -173,7 +183,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int pr = xcd + kNumXcds * (k / a.nqt);                      // pair in longest-first order
     const int qt = a.nqt - 1 - (k % a.nqt);
     const int g = pr % a.H;
-    const int c = __builtin_amdgcn_readfirstlane(nc <= kMaxSortedChunks ? s_order[pr / a.H] : pr / a.H);
+    const int c = __builtin_amdgcn_readfirstlane(few ? s_order[pr / a.H] : pr / a.H);
     const int G = a.G;
     const int QT = kRows >> a.log2G;              // query positions per tile
 
@@ -182,9 +192,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int hh = lane >> 5;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-    const int qs0 = a.qsl[c];
-    const int Cc = a.qsl[c + 1] - qs0;
-    const int Lc = a.lens[c];
+    const int qs0 = __builtin_amdgcn_readfirstlane(few ? s_qsl[c] : a.qsl[c]);
+    const int Cc = __builtin_amdgcn_readfirstlane(few ? s_qsl[c + 1] : a.qsl[c + 1]) - qs0;
+    const int Lc = __builtin_amdgcn_readfirstlane(few ? s_clen[c] : a.lens[c]);
     const bool bad_chunk = qs0 < 0 || Cc < 0 || Cc > a.max_q || qs0 + Cc > a.total_q || Lc < Cc ||
                            static_cast<int64_t>(Lc) > static_cast<int64_t>(a.maxb) * a.bs;
     const float kNaN = __builtin_nanf("");
@@ -351,9 +361,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int nval = Lc - t * kKT;            // keys of the tile inside the context
         if (nval >= kKT) return;
         __syncthreads();                          // every wave's share of the tile is in LDS
-        for (int e = tid; e < kD * kKT; e += kThreads) {
-            const int d = e / kKT, k = e % kKT;
-            if (k >= nval) sV[buf][d * kKT + 8 * ((k >> 3) ^ ((d >> 1) & 7)) + (k & 7)] = 0;
+        // one 16-byte segment (8 keys of one channel row) per item
+        for (int item = tid; item < kD * (kKT / 8); item += kThreads) {
+            const int d = item / (kKT / 8), s = item % (kKT / 8);
+            const int keep = nval - 8 * s;        // keys of the segment inside the context
+            if (keep >= 8) continue;
+            u32x4* p = reinterpret_cast<u32x4*>(&sV[buf][d * kKT + 8 * (s ^ ((d >> 1) & 7))]);
+            *p = keep <= 0 ? kZero4 : keep_first_bf16(*p, keep);
         }
     };
 
@@ -506,7 +520,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         tile(kt, std::integral_constant<int, 0>{});
         if (kt + 1 < nkt) tile(kt + 1, std::integral_constant<int, 1>{});
     }
-    bad = __syncthreads_or(bad);
+    // bad is the same in every wave: each checks the same ids
 
     // ---- normalise and store: lane holds channels 32 mt + 8 (e / 4) + 4 hh + e % 4 of its row ----
     const float l_tot = l_run + other_half(l_run);
