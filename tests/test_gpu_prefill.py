@@ -118,11 +118,19 @@ def test_prefill_random_configs(seed):
     H = int(rng.integers(1, 5))
     bs = int(2 ** rng.integers(3, 9))
     n_chunks = int(rng.integers(1, 5))
-    D = 128
-    Hq = H * G
     chunks = [int(rng.integers(1, 300)) for _ in range(n_chunks)]
     clens = [c + (0 if rng.random() < 0.25 else int(rng.integers(0, 1500))) for c in chunks]
     _announce(f"prefill random config {seed}: G={G} H={H} bs={bs} chunks={chunks} contexts={clens}")
+    err, got = _run_random_prefill(rng, G, H, bs, chunks, clens)
+    assert np.isfinite(got).all() and err <= TOL, err
+
+
+def _run_random_prefill(rng, G, H, bs, chunks, clens, D=128):
+    # a workload of len(chunks) prefill chunks (chunk s: the last chunks[s]
+    # positions of a context of clens[s] tokens) in a shuffled pool, run by
+    # the library and the oracle; returns (max abs error, library output)
+    n_chunks = len(chunks)
+    Hq = H * G
     need = sum(-(-L // bs) for L in clens)
     N = need + 3
     free_order = rng.permutation(N).astype(np.int32)
@@ -148,7 +156,18 @@ def test_prefill_random_configs(seed):
     st_o, st_l = oracle_run.build(w), lib_run.build(w)
     want = oracle_run.oracle_prefill(w, st_o)
     got = lib_run.prefill(w, st_l).double().cpu().numpy()
-    err = np.max(np.abs(got - want))
+    return float(np.max(np.abs(got - want))), got
+
+
+@pytest.mark.parametrize("n_chunks", [256, 300])
+def test_prefill_many_chunks(n_chunks):
+    # the kernel ranks up to 256 chunks by context length in LDS; beyond that
+    # it takes them in order, reading each chunk's start and length itself
+    rng = np.random.default_rng(3000 + n_chunks)
+    chunks = [int(rng.integers(1, 40)) for _ in range(n_chunks)]
+    clens = [c + int(rng.integers(0, 160)) for c in chunks]
+    _announce(f"prefill {n_chunks} chunks: {sum(chunks)} queries, {sum(clens)} context tokens")
+    err, got = _run_random_prefill(rng, 4, 2, 16, chunks, clens)
     assert np.isfinite(got).all() and err <= TOL, err
 
 
