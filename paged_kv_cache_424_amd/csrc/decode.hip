@@ -16,9 +16,14 @@
 // to cut:
 //   * balanced (partition_size == 0, the default): the (sequence, kv head,
 //     32-token chunk) space is laid end to end and cut into equal ranges, one
-//     per workgroup, so every workgroup streams the same number of bytes
-//     whatever the length mix.  A range may cover the tail of one (sequence,
-//     head), several short ones and the head of the next.  Where the cuts fall
+//     per workgroup, so every workgroup streams about the same number of
+//     bytes whatever the length mix.  A range may cover the tail of one
+//     (sequence, head), several short ones and the head of the next.  Each
+//     (sequence, head) is charged two chunk slots more than it has chunks:
+//     the slots stand for what starting a piece costs (the query load, the
+//     first block-id window, the merge and the partial store), so a range
+//     that starts many pieces streams fewer chunks (measured: 3.7 % faster on
+//     a lognormal batch of 240, 5.7 % on a uniform batch of 64).  Where the cuts fall
 //     depends on every length in the batch (and on the number of compute
 //     units), so a row's rounding may change with the rest of the batch.
 //     The grid is persistent: as many workgroups as the chip holds at once.
@@ -79,6 +84,7 @@ constexpr int kChunk = 32;                              // tokens per wave step
 constexpr int kMinBlock = 8;                            // smallest supported block size
 constexpr int kMaxSeqsPerLaunch = 1024;                 // lengths scanned in LDS per launch
 constexpr int kMinPieceChunks = 4;                      // balanced: at least 128 tokens per range
+constexpr int kPieceSlots = 2;                           // balanced: chunk slots charged per (sequence, head)
 constexpr int kMergeHeads = 8;                          // heads merged per LDS pass (12-wave groups)
 
 // Waves per SIMD the kernel is held to (register budget) and waves per
@@ -553,7 +559,7 @@ __attribute__((amdgpu_waves_per_eu((waves_per_simd<BF16, D>())))) void decode_pa
             const bool ok = L >= 1 && L <= a.max_ctx;
             if (!ok) L = -1;
             if (s < B) s_len[s] = L;
-            cnt[i] = ok ? (L + kChunk - 1) / kChunk : 0;      // chunks per head
+            cnt[i] = ok ? (L + kChunk - 1) / kChunk + kPieceSlots : 0;   // chunk slots per head
             sum += cnt[i];
         }
         int tot;
@@ -577,9 +583,10 @@ __attribute__((amdgpu_waves_per_eu((waves_per_simd<BF16, D>())))) void decode_pa
             for (int h = tid; h < a.Hq; h += NT) a.ws_np[static_cast<int64_t>(s) * a.Hq + h] = 0;
     }
 
-    // Ranges of Cw chunks over the (sequence, kv head, chunk) space, laid out
-    // sequence by sequence and head by head.  The workgroup index is remapped
-    // so that neighbouring ranges run on the same XCD.
+    // Ranges of Cw chunk slots over the (sequence, kv head, slot) space, laid
+    // out sequence by sequence and head by head; a (sequence, head) has
+    // kPieceSlots slots with no chunk, then its chunks.  The workgroup index
+    // is remapped so that neighbouring ranges run on the same XCD.
     const int64_t T = static_cast<int64_t>(H) * s_cum[B];
     const int64_t grid = gridDim.x;
     const int64_t Cw = max(static_cast<int64_t>(kMinPieceChunks), (T + grid - 1) / grid);
@@ -590,7 +597,8 @@ __attribute__((amdgpu_waves_per_eu((waves_per_simd<BF16, D>())))) void decode_pa
     int s = find_seq(s_cum, B, static_cast<int>(pos / H));
     if constexpr (APPEND) {
         // The range holds the last chunk of every (sequence, head) it ends
-        // inside: store those newest tokens before the first piece, outside the
+        // inside (the last slot is always a chunk): store those newest tokens
+        // before the first piece, outside the
         // piece loop, so that loop keeps the plain kernel's registers.
         int64_t p2 = pos;
         int s2 = s;
@@ -607,16 +615,20 @@ __attribute__((amdgpu_waves_per_eu((waves_per_simd<BF16, D>())))) void decode_pa
         fence_pending = true;
     }
     while (pos < end) {
-        const int n = s_cum[s + 1] - s_cum[s];          // chunks per head of sequence s
+        const int n = s_cum[s + 1] - s_cum[s];          // slots per head of sequence s
         const int64_t base = static_cast<int64_t>(H) * s_cum[s];
         const int g = static_cast<int>((pos - base) / n);
         const int off = static_cast<int>((pos - base) % n);
         const int take = static_cast<int>(min(static_cast<int64_t>(n - off), end - pos));
         const int64_t start_sg = base + static_cast<int64_t>(g) * n;
-        const int64_t first = start_sg / Cw;
-        const int64_t last = (start_sg + n - 1) / Cw;
-        process(s, g, s_len[s], off, off + take, static_cast<int>(wr - first),
-                static_cast<int>(last - first + 1));
+        // chunks [c0, c1) of the (sequence, head) fall in this range; pieces
+        // are the ranges that hold any of its chunks
+        const int c0 = max(off, kPieceSlots) - kPieceSlots, c1 = off + take - kPieceSlots;
+        if (c1 > c0) {
+            const int64_t first = (start_sg + kPieceSlots) / Cw;
+            const int64_t last = (start_sg + n - 1) / Cw;
+            process(s, g, s_len[s], c0, c1, static_cast<int>(wr - first), static_cast<int>(last - first + 1));
+        }
         pos += take;
         while (s < B && pos >= static_cast<int64_t>(H) * s_cum[s + 1]) ++s;
     }
@@ -734,8 +746,8 @@ struct Plan {
 };
 
 // Piece slots per (sequence, head): fixed partitions need ceil(max_ctx / P);
-// a balanced range of >= kMinPieceChunks chunks cuts a head of n chunks into
-// at most ceil(n / kMinPieceChunks) + 1 pieces.
+// balanced ranges of >= kMinPieceChunks chunk slots cut a head's n chunks (n
+// consecutive slots) into at most ceil(n / kMinPieceChunks) + 1 pieces.
 int32_t piece_slots(int32_t max_context_len, int32_t part_chunks) {
     const int64_t nch = (static_cast<int64_t>(max_context_len) + kChunk - 1) / kChunk;
     if (part_chunks > 0) return static_cast<int32_t>((nch + part_chunks - 1) / part_chunks);
@@ -881,7 +893,8 @@ int launch_partitions(const DecodeArgs& a0, int32_t num_seqs, const Plan& c, hip
             if (rc != PA_OK) return rc;
             if (per_cu < 1) return PA_ERR_UNSUPPORTED;
             const int64_t nch = (static_cast<int64_t>(a.max_ctx) + kChunk - 1) / kChunk;
-            const int64_t items = static_cast<int64_t>(nb) * a.H * ((nch + kMinPieceChunks - 1) / kMinPieceChunks);
+            const int64_t items =
+                static_cast<int64_t>(nb) * a.H * ((nch + kPieceSlots + kMinPieceChunks - 1) / kMinPieceChunks);
             grid = std::max<int64_t>(1, std::min<int64_t>(static_cast<int64_t>(per_cu) * cus, items));
         }
         rc = launch_kernel_timed(kernel, dim3(static_cast<uint32_t>(grid)), dim3(64 * waves), lds, st,

@@ -24,8 +24,8 @@ def _announce(msg):
 @pytest.mark.parametrize("name,part,small", [("c2", 0, True), ("c2", 512, True), ("c3", 256, True),
                                              ("c1", 128, True), ("c2", 0, False)])
 def test_decode_graph_replays_match_eager(name, part, small):
-    # the full-size batch runs the balanced split with dynamic cells: each
-    # replay must find its cell counters reset by the one before
+    # replays of a captured decode (fixed partitions and the balanced split,
+    # small and full size) must match the eager result every time
     _announce(f"graph decode {name} part {part} small {small}")
     w = workloads.make(name, small=small)
     st = lib_run.build(w)
