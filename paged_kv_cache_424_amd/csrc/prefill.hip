@@ -237,13 +237,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
     // ---- block ids: tile t touches blocks (64 t) / bs + [0, n_ids) ----
     const int bs = a.bs;
-    const int n_ids = bs >= kKT ? 1 : kKT / bs;
-    const int nblk = (Lc + bs - 1) / bs;
+    const int log2bs = a.log2bs;                  // block sizes are powers of two
+    const int n_ids = bs >= kKT ? 1 : kKT >> log2bs;
+    const int nblk = (Lc + bs - 1) >> log2bs;
     const int32_t* trow = a.tables + static_cast<int64_t>(c) * a.maxb;
     int bad = 0;                                  // the same in every lane
     // The table entry of block i of tile t (clamped to the last block of the
     // context: any valid block, masked later).
-    auto block_index = [&](int t, int i) { return (t * kKT) / bs + i; };
+    auto block_index = [&](int t, int i) { return ((t * kKT) >> log2bs) + i; };
     auto raw_block_id = [&](int b) { return trow[min(b, nblk - 1)]; };   // nblk >= 1
 
     // ---- tile loader: global -> LDS directly (no registers), 16 bytes per lane ----
@@ -258,7 +259,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // boundary, so each segment's block slot and in-block offset are the same
     // for every tile and are computed once here; larger blocks add the tile's
     // offset inside its block.
-    const int log2bs = a.log2bs;
     const bool big_blocks = bs > kKT;
     const int64_t tile_bytes = static_cast<int64_t>(a.H) * bs * kD * 2;
     const char* kbase = reinterpret_cast<const char*>(a.kc) + static_cast<int64_t>(g) * bs * kD * 2;
@@ -451,13 +451,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         // element e of tile t holds key base + 32 t + 16 (e / 8) + 8 hh + e % 8
         if (base + kKT - 1 > wave_min_pos) {
+            // key <= rowpos, with the element's constant part of the key on the left
+            const int lim = rowpos - base - 8 * hh;
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int key = base + 32 * t + 16 * (e >> 3) + 8 * hh + (e & 7);
-                    st[t][e] = key <= rowpos ? st[t][e] : -INFINITY;
-                }
+                for (int e = 0; e < 16; ++e)
+                    st[t][e] = 32 * t + 16 * (e >> 3) + (e & 7) <= lim ? st[t][e] : -INFINITY;
         }
         // ---- online softmax of the row (this lane and lane ^ 32 share it) ----
         float mx = st[0][0];
