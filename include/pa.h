@@ -280,7 +280,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *   context_lens: device int32 [num_seqs]; L counts the newest token.
  *   max_context_len: an upper bound of every L, used to size the grid.
  *   partition_size: 0 for the balanced split -- the 32-token chunks of all
- *                 (sequence, kv head) pairs are cut into equal ranges, one per
+ *                 (sequence, kv head) pairs, each pair charged two chunks more
+ *                 for starting a piece, are cut into equal ranges, one per
  *                 workgroup the chip holds at once, so the cut points (and the
  *                 fp32 rounding order of a row) depend on the whole batch and
  *                 the device's compute-unit count; or P > 0, a multiple of 32,
