@@ -449,6 +449,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        // The first 32-key half's V fragments are read now, so that their LDS
+        // latency is spent on the mask, the maximum and the weights (read next
+        // to their MFMAs, as the compiler placed them, each stalled on its
+        // read); the second half's take the same registers once the first
+        // half's MFMAs have issued.
+        u32x4 vf[kMT][2];
+#pragma unroll
+        for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                vf[mt][kb] = *reinterpret_cast<const u32x4*>(vfp[0][kb] + buf * kD * kKT + 32 * mt * kKT);
+        __builtin_amdgcn_sched_barrier(0);
         // element e of tile t holds key base + 32 t + 16 (e / 8) + 8 hh + e % 8
         if (base + kKT - 1 > wave_min_pos) {
             // key <= rowpos, with the element's constant part of the key on the left
@@ -500,12 +512,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
                     // keys base + 8 (hh + 4 t + 2 kb) .. +7 of channel 32 mt + col
-                    const u32x4 vf =
-                        *reinterpret_cast<const u32x4*>(vfp[t][kb] + buf * kD * kKT + 32 * mt * kKT);
-                    acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), pb[kb], acc[mt], 0, 0, 0);
+                    acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf[mt][kb]), pb[kb], acc[mt], 0, 0, 0);
+                    if (t == 0)
+                        vf[mt][kb] = *reinterpret_cast<const u32x4*>(vfp[1][kb] + buf * kD * kKT + 32 * mt * kKT);
                 }
             }
         }
+        // the wait for tile kt + 1's loads stays behind every value MFMA
+        __builtin_amdgcn_sched_barrier(0);
         wait_loads();                             // this wave's share of tile kt + 1 is in LDS
         // The id of tile kt + 2 was loaded after tile kt + 1's loads, so its
         // check needs them all to have landed: keep it behind the wait, where
