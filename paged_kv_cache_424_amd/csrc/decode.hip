@@ -712,33 +712,38 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-template <int D>
+// KPRE partial rows (and, with MLPRE, the first 64 (max, sum) pairs) are
+// loaded together with the piece count, before it is known, so a head with few
+// pieces costs one round trip to memory.  That pays where most heads have
+// several pieces (fixed partitions of long contexts); under the balanced split
+// most heads are a single piece, whose speculative loads are wasted bytes, so
+// the host takes fewer there.  All speculative slots lie inside the workspace;
+// the ones past the count hold leftovers and are never used (selected away,
+// not multiplied by zero, as they may be NaN).
+template <int D, int KPRE, bool MLPRE>
 __global__ __launch_bounds__(64 * kReduceWaves) void decode_reduce_kernel(void* out, int out_bf16,
                                                                          const float* __restrict__ ws_acc,
                                                                          const float2* __restrict__ ws_ml,
                                                                          const int32_t* __restrict__ ws_np,
                                                                          int64_t pairs, int32_t P) {
     constexpr int CPL = D / 64;                   // channels per lane
-    constexpr int kPre = 4;                       // partial rows loaded before the piece count
+    constexpr int kPre = KPRE;                    // partial rows loaded before the piece count
     const int lane = threadIdx.x & 63;
     const int64_t pair = static_cast<int64_t>(blockIdx.x) * kReduceWaves + (threadIdx.x >> 6);
     if (pair >= pairs) return;
-    // The piece count, the first 64 (max, sum) pairs and the first kPre partial
-    // rows are loaded together, before the count is known, so a head with few
-    // pieces costs one round trip to memory.  All those slots lie inside the
-    // workspace; the ones past the count hold leftovers and are never used
-    // (selected away, not multiplied by zero, as they may be NaN).
     const int np_raw = ws_np[pair];
     const float2* ml = ws_ml + pair * P;
-    const float2 ml0 = lane < P ? ml[lane] : make_float2(-INFINITY, 0.f);
+    float2 ml0 = make_float2(-INFINITY, 0.f);
+    if constexpr (MLPRE) ml0 = lane < P ? ml[lane] : ml0;
     const float* accp = ws_acc + pair * P * D + lane;
-    float pre[kPre][CPL];
+    float pre[kPre > 0 ? kPre : 1][CPL];
 #pragma unroll
     for (int u = 0; u < kPre; ++u)
 #pragma unroll
         for (int c = 0; c < CPL; ++c) pre[u][c] = u < P ? accp[static_cast<int64_t>(u) * D + 64 * c] : 0.f;
     const int np = min(np_raw, P);
     if (np <= 1) return;                          // final already, or NaN written
+    if constexpr (!MLPRE) ml0 = lane < np ? ml[lane] : ml0;
     float m = lane < np ? ml0.x : -INFINITY;
     for (int i = lane + 64; i < np; i += 64) m = fmaxf(m, ml[i].x);
     const float M = wave_max(m);
@@ -1104,7 +1109,14 @@ int pa_decode_reduce(void* out, int32_t out_dtype, const int32_t* context_lens, 
     const int64_t pairs = static_cast<int64_t>(num_seqs) * num_q_heads;
     const int64_t grid = (pairs + kReduceWaves - 1) / kReduceWaves;
     if (grid > INT32_MAX) return PA_ERR_UNSUPPORTED;
-    const auto kernel = head_dim == 128 ? decode_reduce_kernel<128> : decode_reduce_kernel<64>;
+    // fixed partitions: four rows and the (max, sum) pairs ahead of the count;
+    // balanced split: nothing ahead of it (a lognormal batch of 240, caches
+    // cold: 11.0 us against 18.8 us with the fixed partitions' choice, 13.1 us
+    // with one row ahead)
+    const auto kernel = part_chunks > 0 ? (head_dim == 128 ? decode_reduce_kernel<128, 4, true>
+                                                           : decode_reduce_kernel<64, 4, true>)
+                                        : (head_dim == 128 ? decode_reduce_kernel<128, 0, false>
+                                                           : decode_reduce_kernel<64, 0, false>);
     return launch_kernel(kernel, dim3(static_cast<uint32_t>(grid)), dim3(64 * kReduceWaves), 0,
                          static_cast<hipStream_t>(stream), out, out_dtype == PA_BF16,
                          reinterpret_cast<const float*>(wsb + ws.acc),
