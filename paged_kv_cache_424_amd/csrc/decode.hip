@@ -699,6 +699,7 @@ __attribute__((amdgpu_waves_per_eu((waves_per_simd<BF16, D>())))) void decode_pa
 // ratio.  Lane i owns channels i, i + 64 (D = 128) or i (D = 64); the pieces
 // are summed in a fixed order, so the result does not depend on timing.
 constexpr int kReduceWaves = 4;
+constexpr int kReduceWgPieces = 16;     // fixed partitions allowing this many pieces per head or more: a workgroup per head
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -795,6 +796,81 @@ __global__ __launch_bounds__(64 * kReduceWaves) void decode_reduce_kernel(void* 
     for (int c = 0; c < CPL; ++c) {
         const float v = ((o[0][c] + o[1][c]) + (o[2][c] + o[3][c])) * inv;
         const int64_t idx = pair * D + lane + 64 * c;
+        if (out_bf16)
+            static_cast<__bf16*>(out)[idx] = static_cast<__bf16>(v);
+        else
+            static_cast<float*>(out)[idx] = v;
+    }
+}
+
+// Many pieces per head (fixed partitions of long contexts): one 4-wave
+// workgroup per (sequence, query head), so a batch of few long sequences still
+// spreads its merge over the chip.  Every wave finds the largest piece max M
+// and the denominator over all pieces itself (lanes take pieces, 64 at a
+// time); wave w sums the weighted partial rows of pieces w, w + 4, w + 8, ...,
+// four rows in flight per lane, and the four sums are added through LDS in
+// wave order, so the result does not depend on timing.
+template <int D>
+__global__ __launch_bounds__(64 * kReduceWaves) void decode_reduce_wg_kernel(void* out, int out_bf16,
+                                                                            const float* __restrict__ ws_acc,
+                                                                            const float2* __restrict__ ws_ml,
+                                                                            const int32_t* __restrict__ ws_np,
+                                                                            int64_t pairs, int32_t P) {
+    constexpr int CPL = D / 64;                   // channels per lane
+    constexpr int NW = kReduceWaves;
+    __shared__ float s_o[NW][D];
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int64_t pair = blockIdx.x;
+    if (pair >= pairs) return;
+    const int np = min(ws_np[pair], P);
+    if (np <= 1) return;                          // final already, or NaN written (the whole workgroup)
+    const float2* ml = ws_ml + pair * P;
+    float m = -INFINITY;
+    for (int i = lane; i < np; i += 64) m = fmaxf(m, ml[i].x);
+    const float M = wave_max(m);
+    float dp = 0.f;
+    for (int i = lane; i < np; i += 64) {
+        const float2 v = ml[i];
+        dp += __builtin_amdgcn_exp2f(v.x - M) * v.y;
+    }
+    const float den = wave_sum(dp);
+    const float* accp = ws_acc + pair * P * D + lane;
+    float o[4][CPL];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) o[u][c] = 0.f;
+    for (int b0 = 0; b0 < np; b0 += 64) {
+        const int nb = min(64, np - b0);
+        const float fl = lane < nb ? __builtin_amdgcn_exp2f(ml[b0 + lane].x - M) : 0.f;
+        int k = w;
+        for (; k + 3 * NW < nb; k += 4 * NW) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float f = __shfl(fl, k + u * NW);
+                const float* src = accp + static_cast<int64_t>(b0 + k + u * NW) * D;
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) o[u][c] += f * src[64 * c];
+            }
+        }
+        for (; k < nb; k += NW) {
+            const float f = __shfl(fl, k);
+            const float* src = accp + static_cast<int64_t>(b0 + k) * D;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) o[0][c] += f * src[64 * c];
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) s_o[w][lane + 64 * c] = (o[0][c] + o[1][c]) + (o[2][c] + o[3][c]);
+    __syncthreads();
+    if (w != 0) return;
+    const float inv = 1.f / den;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const int i = lane + 64 * c;
+        const float v = ((s_o[0][i] + s_o[1][i]) + (s_o[2][i] + s_o[3][i])) * inv;
+        const int64_t idx = pair * D + i;
         if (out_bf16)
             static_cast<__bf16*>(out)[idx] = static_cast<__bf16>(v);
         else
@@ -1107,6 +1183,16 @@ int pa_decode_reduce(void* out, int32_t out_dtype, const int32_t* context_lens, 
     if (!out || !workspace || workspace_bytes < ws.total) return PA_ERR_INVALID_ARG;
     const char* wsb = static_cast<const char*>(workspace);
     const int64_t pairs = static_cast<int64_t>(num_seqs) * num_q_heads;
+    if (part_chunks > 0 && pmax >= kReduceWgPieces) {
+        // heads of up to pmax pieces: a workgroup per (sequence, query head)
+        if (pairs > INT32_MAX) return PA_ERR_UNSUPPORTED;
+        const auto kernel = head_dim == 128 ? decode_reduce_wg_kernel<128> : decode_reduce_wg_kernel<64>;
+        return launch_kernel(kernel, dim3(static_cast<uint32_t>(pairs)), dim3(64 * kReduceWaves), 0,
+                             static_cast<hipStream_t>(stream), out, out_dtype == PA_BF16,
+                             reinterpret_cast<const float*>(wsb + ws.acc),
+                             reinterpret_cast<const float2*>(wsb + ws.ml),
+                             reinterpret_cast<const int32_t*>(wsb + ws.np), pairs, pmax);
+    }
     const int64_t grid = (pairs + kReduceWaves - 1) / kReduceWaves;
     if (grid > INT32_MAX) return PA_ERR_UNSUPPORTED;
     // fixed partitions: four rows and the (max, sum) pairs ahead of the count;
