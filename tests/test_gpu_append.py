@@ -55,8 +55,18 @@ def _many():
     return workloads.configs._decode_batch_from(rng, "many", "bf16", lens, 8, 2, 64, 16)
 
 
+def _many_g16():
+    # 1,000 short sequences with 16-head groups at head_dim 128: the balanced
+    # split's ranges then hold more pieces than the decode holds back at once
+    # (three of 16 x 128), so held-back results are stored both when the
+    # buffer fills and at the end of a range, next to the newest-token stores
+    rng = np.random.default_rng(13)
+    lens = rng.integers(1, 120, size=1000)
+    return workloads.configs._decode_batch_from(rng, "many_g16", "bf16", lens, 32, 2, 128, 16)
+
+
 CASES = [("c1", lambda: workloads.make("c1")), ("c2", lambda: workloads.make("c2", small=True)),
-         ("c3", lambda: workloads.make("c3", small=True)), ("many", _many)]
+         ("c3", lambda: workloads.make("c3", small=True)), ("many", _many), ("many_g16", _many_g16)]
 
 
 @pytest.mark.parametrize("part", [512, 0])
