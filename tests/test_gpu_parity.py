@@ -79,10 +79,14 @@ def test_partition_sizes(case, part):
     assert np.max(np.abs(got - want)) <= BUDGET[w.dtype]
 
 
-def test_bf16_output(case):
+@pytest.mark.parametrize("part", [0, 32])
+def test_bf16_output(case, part):
+    # both store paths of the output: the balanced split's held-back results
+    # and, with 32-token partitions (up to 16 or more pieces a head), the
+    # reduce's workgroup per head
     name, w, st_o, st_l = case
     want = oracle_run.oracle_decode(w, st_o)
-    got = lib_run.decode(w, st_l, out_dtype=torch.bfloat16).double().cpu().numpy()
+    got = lib_run.decode(w, st_l, partition_size=part, out_dtype=torch.bfloat16).double().cpu().numpy()
     # rounding the output to bf16 adds at most half an ulp of |out|
     assert np.all(np.abs(got - want) <= BUDGET[w.dtype] + np.abs(want) * 2.0 ** -8)
 
